@@ -1,0 +1,186 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) VAR-Q packed KV-cache library.
+ *
+ * VAR-Q ("VAR-Q: Tuning-Free KV Cache Quantization for Visual Autoregressive
+ * Image and Video Generation", abstract and key contributions) observes that
+ * block-by-block visual AR decoding produces KV caches whose massive-value
+ * channels are persistent inside a (block, channel) cell and shift across
+ * cells, and quantizes in groups along exactly those two axes, taking the
+ * block boundaries from the generation loop; bit-packing kernels make the
+ * memory saving real at run time.  This library is that hot path on one GPU:
+ *
+ *   kvq_quantize_block  quantize one freshly decoded block of K and V with an
+ *                       asymmetric min/max grid per (sequence, block, head,
+ *                       channel) group and bit-pack the codes into the cache;
+ *   kvq_pack            the bit-packing step alone (codes given one per byte);
+ *   kvq_attend_packed   block-causal attention of the block's queries over the
+ *                       packed cache of blocks 0..k, dequantizing on the fly;
+ *   kvq_bytes           the cache's byte accounting (host only).
+ *
+ * Conventions shared by every call
+ *   - All buffers are owned by the caller; the library allocates nothing and
+ *     keeps no state, so calls are reentrant.  Device pointers must be
+ *     16-byte aligned device memory (else KVQ_E_INVAL).
+ *   - Calls are asynchronous on `stream` (NULL = the null stream); argument
+ *     errors are returned synchronously before anything is launched; a launch
+ *     failure is returned as KVQ_E_DEVICE.
+ *   - Tensor layouts (row-major, innermost last):
+ *       block input  x[B][n_k][H][D]      K, V or Q of block k (n_k tokens)
+ *       codes        [B][H][T][R]         T = sum of all block_tokens,
+ *                                         R = ceil(bits * D / 8) bytes per row
+ *       zero, scale  [B][H][NB][D]        IEEE binary16 bit patterns
+ *       attention out[B][n_k][H][D]       fp32
+ *     Block k's rows are tokens [off_k, off_k + n_k) with off_k the sum of
+ *     block_tokens[0..k-1].
+ *   - Quantizer of one group with values x_i (binary32) and L = 2^bits - 1:
+ *       z = largest binary16 <= min_i x_i,
+ *       s = smallest binary16 >= fp32(fp32(max_i x_i - z) / L),
+ *       code_i = clamp(round_half_even(fp32(fp32(x_i - z) * fp32(1/s))), 0, L)
+ *       (all codes 0 when s = 0), dequantized value fma(code, s, z).
+ *     A zero extreme is taken as +0.  Every value lies on or inside
+ *     [z, z + L*s], so |x - x_hat| <= s/2 up to binary32 rounding.
+ *   - Packing: each (sequence, head, token) row of D codes is an LSB-first bit
+ *     stream; code d occupies stream bits [bits*d, bits*d + bits) and stream
+ *     bit j is bit (j mod 8) of byte floor(j/8), so 3-bit codes 2 and 5 of
+ *     every eight straddle byte boundaries.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_MAX_BLOCKS 64
+
+/* return codes */
+#define KVQ_OK 0
+#define KVQ_E_INVAL (-1)       /* bad argument, layout, pointer or alignment */
+#define KVQ_E_UNSUPPORTED (-2) /* valid, but not built for this GPU path */
+#define KVQ_E_DEVICE (-3)      /* HIP launch / runtime failure */
+
+/* device status bits OR-ed into *status_dev by kvq_quantize_block */
+#define KVQ_S_NONFINITE 1 /* a NaN or +-inf input value */
+#define KVQ_S_RANGE 2     /* a group extreme outside +-65504 (binary16 range) */
+
+/* source dtypes */
+#define KVQ_F32 0
+#define KVQ_BF16 1
+
+/*
+ * Cache geometry, a plain value owned by the caller.
+ *   batch       sequences B (>= 1)
+ *   heads       H (>= 1)
+ *   head_dim    D (multiple of 8; the GPU kernels are built for 64 and 128)
+ *   bits        code width: 3 or 4 on the GPU (the byte accounting takes 1..8)
+ *   n_blocks    NB, number of decode blocks (1..KVQ_MAX_BLOCKS)
+ *   pack_mode   0 = dense rows (the only mode built)
+ *   block_tokens[k]  tokens of block k (>= 1), e.g. s*s for next-scale
+ *                    prediction at scale s, or a frame's tokens for video
+ */
+typedef struct {
+  int32_t batch, heads, head_dim, bits, n_blocks, pack_mode;
+  int32_t block_tokens[KVQ_MAX_BLOCKS];
+} kvq_layout;
+
+/* one packed cache (K or V of one layer); device pointers */
+typedef struct {
+  uint8_t* codes;  /* [B][H][T][R] */
+  uint16_t* zero;  /* [B][H][NB][D] binary16 */
+  uint16_t* scale; /* [B][H][NB][D] binary16 */
+} kvq_cache;
+
+typedef struct {
+  const uint8_t* codes;
+  const uint16_t* zero;
+  const uint16_t* scale;
+} kvq_cache_const;
+
+/*
+ * kvq_bytes -- bytes held by one (layer, K or V) cache once blocks
+ * 0..n_filled-1 are stored: code_bytes = B*H*T*R with T = sum of their
+ * block_tokens, stat_bytes = B*H*n_filled*D*4 (one binary16 zero + one binary16
+ * step per (block, channel) group).  With n_filled = n_blocks these are the
+ * allocation sizes of codes and of zero+scale together.  Host only, pure.
+ * Follows the KV-memory accounting of the VAR-Q results table (VAR-d20 at 2x128
+ * sequences: 16.60 -> 4.64 GiB at INT4, 72.06% saving).
+ * Returns KVQ_OK or KVQ_E_INVAL (bad layout, n_filled out of [0, NB], NULL out).
+ */
+int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
+              uint64_t* stat_bytes);
+
+/*
+ * kvq_quantize_block -- quantize block `block` of K and V of one layer and
+ * store it packed (VAR-Q: groups keyed on (block, channel), block boundary
+ * handed over by the generation loop; then bit-packing).
+ *   k_src, v_src  [B][n_k][H][D], dtype src_dtype (KVQ_F32 or KVQ_BF16)
+ *   k_cache, v_cache  caches of the layer; only rows [off_k, off_k + n_k) of
+ *                 every (b, h) and stats slot k are written, no other byte
+ *   status_dev    NULL, or a device int32 into which KVQ_S_* bits are OR-ed
+ *                 (read it after synchronizing the stream).  With NULL the
+ *                 inputs are not screened and a non-finite or out-of-range
+ *                 input leaves that group's outputs undefined.
+ * Errors: KVQ_E_INVAL (layout, block, dtype, NULL or misaligned pointer),
+ * KVQ_E_UNSUPPORTED (bits or head_dim not built), KVQ_E_DEVICE.
+ */
+int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtype,
+                       const void* k_src, const void* v_src, kvq_cache k_cache,
+                       kvq_cache v_cache, int32_t* status_dev, hipStream_t stream);
+
+/*
+ * kvq_pack -- the bit-packing step on its own: rows of `row_len` codes, one
+ * code per byte (only the low `bits` bits of each byte are used), packed into
+ * rows of ceil(bits*row_len/8) bytes at dst + r*dst_row_stride, bytes between
+ * rows untouched.  Same bit layout as the cache rows written by
+ * kvq_quantize_block ("bit-packing kernels", VAR-Q abstract).
+ *   bits 1..8, pack_mode 0, n_rows >= 0, row_len >= 1,
+ *   dst_row_stride >= ceil(bits*row_len/8).
+ * codes/dst: device pointers (16-byte aligned).
+ */
+int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,
+             int32_t row_len, uint8_t* dst, int64_t dst_row_stride, hipStream_t stream);
+
+/*
+ * kvq_attend_packed -- block-causal attention for block k's queries:
+ *   out[b][i][h][:] = softmax_t(scale * q[b][i][h] . k_hat[b][h][t]) v_hat[b][h][t]
+ * over every token t of blocks 0..k (the whole prefix, no mask inside block
+ * k), where k_hat / v_hat are the dequantized cache values fma(code, s, z)
+ * formed in registers from the packed rows (block-by-block decoding, VAR-Q
+ * abstract; "quantize, then attend": block k's own keys are read packed).
+ *   q_bf16   [B][n_k][H][D] bfloat16 bit patterns
+ *   scale    softmax scale; <= 0 selects 1/sqrt(D)
+ *   out      [B][n_k][H][D] fp32
+ * Accuracy: max|out - exact| <= 2e-3 * max|exact| per call on VAR-shaped data
+ * (QK^T as two bf16 MFMA products of a hi/lo split of k_hat, P and v_hat in
+ * fp16, fp32 accumulation and softmax).
+ * Errors as kvq_quantize_block.
+ */
+int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
+                      kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
+                      float* out, hipStream_t stream);
+
+/* ---- test and measurement helpers (not on the decode path) -------------- */
+
+/* inverse of kvq_pack: codes[r][j] = code j of packed row r (one per byte) */
+int kvq_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_row_stride,
+               int64_t n_rows, int32_t row_len, uint8_t* codes, hipStream_t stream);
+
+/* dequantized cache of blocks 0..n_filled-1: out[B][H][T][D] fp32 with
+ * T = off_{n_filled}; each value fma(code, s, z) as in the attention */
+int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const cache,
+                   float* out, hipStream_t stream);
+
+/* plain streaming copy of n_bytes (multiple of 16): measures the achievable
+ * HBM bandwidth and calibrates the memory counters */
+int kvq_stream_copy(const void* src, void* dst, uint64_t n_bytes, hipStream_t stream);
+
+/* version string of the library */
+const char* kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

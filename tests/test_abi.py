@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/kvq.h declares, rejects bad arguments before touching a
+device, and its byte accounting agrees with the oracle's (an independent
+implementation pinned to the pages' table)."""
+import ctypes as C
+
+import pytest
+
+import varq_inputs as vi
+import visual_autoregressive_kv_amd as K
+from visual_autoregressive_kv_amd import kvq as kb
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.lib()
+    names = K.header_symbols()
+    assert set(names) >= {"kvq_quantize_block", "kvq_pack", "kvq_attend_packed", "kvq_bytes"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in K.kvq_version()
+
+
+@pytest.mark.parametrize("wl", list(vi.WORKLOADS.values()), ids=list(vi.WORKLOADS))
+def test_bytes_match_oracle(oracle, wl):
+    Lg = K.make_layout(wl.batch, wl.heads, wl.head_dim, wl.bits, wl.blocks)
+    Lo = oracle.layout_of(wl)
+    for n_filled in range(len(wl.blocks) + 1):
+        assert K.kvq_bytes(Lg, n_filled) == oracle.nbytes(Lo, n_filled)
+
+
+def test_bytes_rejects_bad_input():
+    L = K.make_layout(2, 3, 64, 4, (1, 4))
+    with pytest.raises(K.KvqError):
+        K.kvq_bytes(L, 3)
+    with pytest.raises(K.KvqError):
+        K.kvq_bytes(K.make_layout(2, 3, 60, 4, (1, 4)), 1)  # head_dim % 8
+    with pytest.raises(K.KvqError):
+        K.kvq_bytes(K.make_layout(2, 3, 64, 9, (1, 4)), 1)  # bits
+    with pytest.raises(K.KvqError):
+        K.kvq_bytes(K.make_layout(0, 3, 64, 4, (1, 4)), 1)
+    with pytest.raises(K.KvqError):
+        K.kvq_bytes(K.make_layout(1, 3, 64, 4, (1, 0)), 1)
+    assert K.lib().kvq_bytes(C.byref(L), 1, None, None) == kb.E_INVAL
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below
+                # must return before any launch
+
+
+def _cache(p=FAKE):
+    return kb.Cache(p, p, p)
+
+
+def test_quantize_argument_errors_return_before_launch():
+    lib = K.lib()
+    L = K.make_layout(2, 3, 64, 4, (1, 4, 9))
+    E = kb.E_INVAL
+    q = lib.kvq_quantize_block
+    assert q(C.byref(L), 3, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == E
+    assert q(C.byref(L), -1, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == E
+    assert q(C.byref(L), 0, 7, FAKE, FAKE, _cache(), _cache(), None, None) == E
+    assert q(C.byref(L), 0, kb.BF16, None, FAKE, _cache(), _cache(), None, None) == E
+    assert q(C.byref(L), 0, kb.BF16, FAKE + 8, FAKE, _cache(), _cache(), None, None) == E
+    assert q(C.byref(L), 0, kb.BF16, FAKE, FAKE, kb.Cache(FAKE, None, FAKE), _cache(),
+             None, None) == E
+    assert q(C.byref(L), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(FAKE + 4), None, None) == E
+    assert q(C.byref(L), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), FAKE + 2, None) == E
+    assert q(None, 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == E
+    # valid but not built for the GPU: 5-bit codes, head_dim 32
+    L5 = K.make_layout(2, 3, 64, 5, (1, 4, 9))
+    assert q(C.byref(L5), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == \
+        kb.E_UNSUPPORTED
+    L32 = K.make_layout(2, 3, 32, 4, (1, 4, 9))
+    assert q(C.byref(L32), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == \
+        kb.E_UNSUPPORTED
+
+
+def test_attend_and_pack_argument_errors_return_before_launch():
+    lib = K.lib()
+    L = K.make_layout(2, 3, 64, 3, (1, 4, 9))
+    E = kb.E_INVAL
+    a = lib.kvq_attend_packed
+    assert a(C.byref(L), 3, FAKE, _cache(), _cache(), 0.0, FAKE, None) == E
+    assert a(C.byref(L), 0, None, _cache(), _cache(), 0.0, FAKE, None) == E
+    assert a(C.byref(L), 0, FAKE, _cache(), _cache(), 0.0, FAKE + 4, None) == E
+    assert a(C.byref(L), 0, FAKE, _cache(), _cache(), float("nan"), FAKE, None) == E
+    assert a(C.byref(L), 0, FAKE, _cache(), _cache(), float("inf"), FAKE, None) == E
+    p = lib.kvq_pack
+    assert p(0, 0, FAKE, 4, 64, FAKE, 32, None) == E      # bits
+    assert p(9, 0, FAKE, 4, 64, FAKE, 72, None) == E
+    assert p(4, 1, FAKE, 4, 64, FAKE, 32, None) == E      # pack_mode
+    assert p(4, 0, FAKE, 4, 64, FAKE, 31, None) == E      # stride < row bytes
+    assert p(3, 0, FAKE, 4, 64, FAKE, 23, None) == E
+    assert p(4, 0, FAKE, -1, 64, FAKE, 32, None) == E
+    assert p(4, 0, None, 4, 64, FAKE, 32, None) == E
+    assert p(4, 0, FAKE, 0, 64, None, 32, None) == kb.OK  # nothing to do
+    u = lib.kvq_unpack
+    assert u(4, 0, FAKE, 31, 4, 64, FAKE, None) == E
+    assert lib.kvq_stream_copy(FAKE, FAKE, 15, None) == E
+    assert lib.kvq_stream_copy(FAKE, FAKE, 0, None) == kb.OK
+
+
+def test_layout_limits():
+    lib = K.lib()
+    L = K.make_layout(2, 3, 64, 4, (1,) * 64)
+    cb, sb = K.kvq_bytes(L, 64)
+    assert cb == 2 * 3 * 64 * 32 and sb == 2 * 3 * 64 * 64 * 4
+    L.n_blocks = 65
+    assert lib.kvq_bytes(C.byref(L), 1, C.byref(C.c_uint64()), C.byref(C.c_uint64())) == \
+        kb.E_INVAL

@@ -1,0 +1,135 @@
+"""GPU parity of kvq_attend_packed against the binary64 CPU oracle:
+max|gpu - oracle| / max|oracle| <= 2e-3 per call, on caches both sides built
+(the GPU cache is first checked bit-exact against the oracle's)."""
+import numpy as np
+import pytest
+import torch
+
+import varq_inputs as vi
+import visual_autoregressive_kv_amd as K
+from gpu_common import ATTN_TOL, DEV, assert_cache_equal, attn_err, fill_both, layouts, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_attend(Lg, block, q_np, kg, vg, scale=0.0):
+    out = torch.full(tuple(q_np.shape), float("nan"), dtype=torch.float32, device=DEV)
+    K.kvq_attend_packed(Lg, block, to_dev(q_np), kg, vg, out, scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_tiny_last_scale(oracle):
+    """The small reference case: last scale's 256 queries over all 680 tokens."""
+    wl = vi.WORKLOADS["var256_tiny_int4"]
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)
+    assert_cache_equal(kg, ko)
+    assert_cache_equal(vg, vo)
+    q = vi.q_block(wl, 0, 9)
+    ref = oracle.attend(Lo, 9, q, ko, vo).astype(np.float64)
+    got = gpu_attend(Lg, 9, q, kg, vg)
+    assert np.isfinite(got).all()
+    err = attn_err(got, ref)
+    assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("name", ["var256_tiny_int4", "var_d20_b128_int4",
+                                  "var_d20_b128_int3_rope", "var_d24_b128_int4"])
+def test_every_scale(oracle, name):
+    wl = vi.WORKLOADS[name]
+    if wl.batch > 2:
+        wl = wl.with_(batch=2)
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl, layer=3)
+    for block in range(len(wl.blocks)):
+        q = vi.q_block(wl, 3, block)
+        ref = oracle.attend(Lo, block, q, ko, vo).astype(np.float64)
+        got = gpu_attend(Lg, block, q, kg, vg)
+        err = attn_err(got, ref)
+        assert err <= ATTN_TOL, (block, err)
+
+
+def test_full_batch_last_scale_sampled(oracle):
+    """VAR-d20 at batch 128, the bench's launch configuration: sampled output rows
+    against single-row oracle evaluations."""
+    wl = vi.WORKLOADS["var_d20_b128_int4"]
+    Lg, Lo = layouts(oracle, wl)
+    kg, vg = K.alloc_cache(Lg), K.alloc_cache(Lg)
+    ko, vo = oracle.alloc_cache(Lo), oracle.alloc_cache(Lo)
+    for j in range(10):
+        kb, vb = vi.kv_block(wl, 0, "k", j), vi.kv_block(wl, 0, "v", j)
+        assert oracle.quantize_block(Lo, j, kb, vb, ko, vo) == 0
+        K.kvq_quantize_block(Lg, j, to_dev(kb), to_dev(vb), kg, vg)
+    torch.cuda.synchronize()
+    assert_cache_equal(kg, ko)
+    assert_cache_equal(vg, vo)
+    rng = np.random.default_rng(0)
+    for block in (9, 6):
+        q = vi.q_block(wl, 0, block)
+        got = gpu_attend(Lg, block, q, kg, vg)
+        assert np.isfinite(got).all()
+        picks = [(int(rng.integers(128)), int(rng.integers(wl.blocks[block])),
+                  int(rng.integers(20))) for _ in range(96)]
+        picks += [(127, wl.blocks[block] - 1, 19), (0, 0, 0)]
+        ref = np.stack([oracle.attend_row(Lo, block, q, ko, vo, b, i, h) for b, i, h in picks])
+        g = np.stack([got[b, i, h] for b, i, h in picks])
+        err = float(np.abs(g - ref).max() / np.abs(ref).max())
+        assert err <= ATTN_TOL, (block, err)
+
+
+def test_video_frames_sampled(oracle):
+    """Next-frame video shape: 40 heads x 128, frames of 1560 tokens (3 frames)."""
+    wl = vi.WORKLOADS["video_16x1560_h40d128_int3"].with_(blocks=(1560, 1560, 1560))
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)
+    q = vi.q_block(wl, 0, 2)
+    got = gpu_attend(Lg, 2, q, kg, vg)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(1)
+    picks = [(0, int(rng.integers(1560)), int(rng.integers(40))) for _ in range(64)]
+    picks += [(0, 1559, 39), (0, 1536, 0), (0, 0, 0)]
+    ref = np.stack([oracle.attend_row(Lo, 2, q, ko, vo, b, i, h) for b, i, h in picks])
+    g = np.stack([got[b, i, h] for b, i, h in picks])
+    err = float(np.abs(g - ref).max() / np.abs(ref).max())
+    assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_ragged_edges(oracle, bits, head_dim):
+    """Query counts off the 32-row tile (1, 7, 33, 257 -> two workgroups per head),
+    prefixes off the 32-key tile, odd batch and heads."""
+    wl = vi.Workload("edge", 1, 3, 3, head_dim, bits, (1, 7, 33, 257, 2), "bf16",
+                     rope=True, seed=11)
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)
+    for block in range(len(wl.blocks)):
+        q = vi.q_block(wl, 0, block)
+        ref = oracle.attend(Lo, block, q, ko, vo).astype(np.float64)
+        got = gpu_attend(Lg, block, q, kg, vg)
+        err = attn_err(got, ref)
+        assert err <= ATTN_TOL, (block, err)
+
+
+def test_explicit_scale_and_determinism(oracle):
+    wl = vi.WORKLOADS["var_d20_b128_int3_rope"].with_(batch=2)
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl, upto=8)
+    q = vi.q_block(wl, 0, 7)
+    ref = oracle.attend(Lo, 7, q, ko, vo, scale=0.05).astype(np.float64)
+    a = gpu_attend(Lg, 7, q, kg, vg, scale=0.05)
+    b = gpu_attend(Lg, 7, q, kg, vg, scale=0.05)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert attn_err(a, ref) <= ATTN_TOL
+
+
+def test_reads_only_the_prefix(oracle):
+    """Garbage in blocks after k (cache bytes and stats) does not change block k's
+    output: the attention reads the packed prefix of blocks 0..k only."""
+    wl = vi.WORKLOADS["var_d20_b128_int4"].with_(batch=2)
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl, upto=7)
+    q = vi.q_block(wl, 0, 6)
+    a = gpu_attend(Lg, 6, q, kg, vg)
+    T = wl.offset(7)
+    for c in (kg, vg):
+        c["codes"][:, :, T:] = 0xFF
+        c["zero"][:, :, 7:] = float("nan")
+        c["scale"][:, :, 7:] = float("inf")
+    b = gpu_attend(Lg, 6, q, kg, vg)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -1,0 +1,253 @@
+// kvq_api.hip -- the extern "C" boundary of libkvq (declared in include/kvq.h).
+// Validates every argument on the host, computes the layout arithmetic and
+// launches the gfx950 kernels on the caller's stream.  Allocates nothing.
+#include <math.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+using namespace kvq;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 46;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int32_t row_bytes(int32_t bits, int32_t d) { return (bits * d + 7) / 8; }
+
+int validate_layout(const kvq_layout* L) {
+  if (!L) return KVQ_E_INVAL;
+  if (L->batch < 1 || L->heads < 1) return KVQ_E_INVAL;
+  if (L->head_dim < 8 || L->head_dim % 8 != 0) return KVQ_E_INVAL;
+  if (L->bits < 1 || L->bits > 8) return KVQ_E_INVAL;
+  if (L->n_blocks < 1 || L->n_blocks > KVQ_MAX_BLOCKS) return KVQ_E_INVAL;
+  if (L->pack_mode != 0) return KVQ_E_INVAL;
+  int64_t T = 0;
+  for (int i = 0; i < L->n_blocks; ++i) {
+    if (L->block_tokens[i] < 1) return KVQ_E_INVAL;
+    T += L->block_tokens[i];
+  }
+  if (T > INT32_MAX) return KVQ_E_INVAL;
+  const int64_t bh = (int64_t)L->batch * L->heads;
+  if (bh > INT32_MAX / 2) return KVQ_E_INVAL;
+  if (bh * T * L->head_dim > kMaxElems) return KVQ_E_INVAL;
+  return KVQ_OK;
+}
+
+// kernels are built for 3/4-bit codes and head_dim 64/128
+int gpu_supported(const kvq_layout* L) {
+  if (L->bits != 3 && L->bits != 4) return KVQ_E_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return KVQ_E_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+int64_t offset_of(const kvq_layout* L, int32_t block) {
+  int64_t off = 0;
+  for (int i = 0; i < block; ++i) off += L->block_tokens[i];
+  return off;
+}
+
+int cache_ok(const kvq_cache& c) {
+  return c.codes && c.zero && c.scale && aligned16(c.codes) && aligned16(c.zero) &&
+         aligned16(c.scale);
+}
+int cache_ok(const kvq_cache_const& c) {
+  return c.codes && c.zero && c.scale && aligned16(c.codes) && aligned16(c.zero) &&
+         aligned16(c.scale);
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE; }
+
+// threads per (tensor, b, h) tile and rows per thread for a block of n rows:
+// the smallest power-of-two group (>= one row of chunks) that covers the block
+// with at most 8 rows per thread; larger blocks stream in passes of 256 x 8
+void pick_tiling(int n, int d, int32_t* gs, int32_t* rpt) {
+  const int cpr = d / 8;
+  for (int g = cpr; g <= 256; g <<= 1) {
+    const int rps = g / cpr;
+    const int r = (n + rps - 1) / rps;
+    if (r <= 8) {
+      *gs = g;
+      *rpt = r;
+      return;
+    }
+  }
+  *gs = 256;
+  *rpt = 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_version(void) { return "kvq 0.1 (gfx950)"; }
+
+int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
+              uint64_t* stat_bytes) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (n_filled < 0 || n_filled > layout->n_blocks || !code_bytes || !stat_bytes)
+    return KVQ_E_INVAL;
+  const uint64_t bh = (uint64_t)layout->batch * (uint64_t)layout->heads;
+  const uint64_t T = (uint64_t)offset_of(layout, n_filled);
+  *code_bytes = bh * T * (uint64_t)row_bytes(layout->bits, layout->head_dim);
+  *stat_bytes = bh * (uint64_t)n_filled * (uint64_t)layout->head_dim * 4u;
+  return KVQ_OK;
+}
+
+int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtype,
+                       const void* k_src, const void* v_src, kvq_cache k_cache,
+                       kvq_cache v_cache, int32_t* status_dev, hipStream_t stream) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (block < 0 || block >= layout->n_blocks) return KVQ_E_INVAL;
+  if (src_dtype != KVQ_F32 && src_dtype != KVQ_BF16) return KVQ_E_INVAL;
+  if (!k_src || !v_src || !aligned16(k_src) || !aligned16(v_src)) return KVQ_E_INVAL;
+  if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
+  if (status_dev && (reinterpret_cast<uintptr_t>(status_dev) & 3)) return KVQ_E_INVAL;
+  const int sup = gpu_supported(layout);
+  if (sup != KVQ_OK) return sup;
+
+  QuantParams p;
+  memset(&p, 0, sizeof(p));
+  p.src[0] = k_src;
+  p.src[1] = v_src;
+  p.codes[0] = k_cache.codes;
+  p.codes[1] = v_cache.codes;
+  p.zero[0] = k_cache.zero;
+  p.zero[1] = v_cache.zero;
+  p.scale[0] = k_cache.scale;
+  p.scale[1] = v_cache.scale;
+  p.status = status_dev;
+  p.BH = layout->batch * layout->heads;
+  p.n_tiles = 2 * (int64_t)p.BH;
+  p.H = layout->heads;
+  p.n = layout->block_tokens[block];
+  p.NB = layout->n_blocks;
+  p.block = block;
+  p.R = row_bytes(layout->bits, layout->head_dim);
+  p.T = offset_of(layout, layout->n_blocks);
+  p.off = offset_of(layout, block);
+  pick_tiling(p.n, layout->head_dim, &p.gs, &p.rpt);
+  return device_status(
+      launch_quantize(p, layout->head_dim, layout->bits, src_dtype == KVQ_F32, stream));
+}
+
+int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,
+             int32_t row_len, uint8_t* dst, int64_t dst_row_stride, hipStream_t stream) {
+  if (bits < 1 || bits > 8 || pack_mode != 0 || n_rows < 0 || row_len < 1) return KVQ_E_INVAL;
+  const int32_t R = row_bytes(bits, row_len);
+  if (dst_row_stride < R) return KVQ_E_INVAL;
+  if (n_rows == 0) return KVQ_OK;
+  if (!codes || !dst || !aligned16(codes) || !aligned16(dst)) return KVQ_E_INVAL;
+  if (n_rows > kMaxElems / row_len) return KVQ_E_INVAL;
+  PackParams p;
+  memset(&p, 0, sizeof(p));
+  p.codes = codes;
+  p.dst = dst;
+  p.n_rows = n_rows;
+  p.dst_stride = dst_row_stride;
+  p.row_len = row_len;
+  p.bits = bits;
+  p.chunks_per_row = (row_len + 7) / 8;
+  p.n_chunks = n_rows * p.chunks_per_row;
+  p.R = R;
+  p.contiguous = (dst_row_stride == R) && (row_len % 8 == 0);
+  return device_status(launch_pack(p, stream));
+}
+
+int kvq_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_row_stride,
+               int64_t n_rows, int32_t row_len, uint8_t* codes, hipStream_t stream) {
+  if (bits < 1 || bits > 8 || pack_mode != 0 || n_rows < 0 || row_len < 1) return KVQ_E_INVAL;
+  if (src_row_stride < row_bytes(bits, row_len)) return KVQ_E_INVAL;
+  if (n_rows == 0) return KVQ_OK;
+  if (!codes || !src || !aligned16(codes) || !aligned16(src)) return KVQ_E_INVAL;
+  if (n_rows > kMaxElems / row_len) return KVQ_E_INVAL;
+  UnpackParams p;
+  memset(&p, 0, sizeof(p));
+  p.src = src;
+  p.codes = codes;
+  p.n_rows = n_rows;
+  p.src_stride = src_row_stride;
+  p.row_len = row_len;
+  p.bits = bits;
+  p.chunks_per_row = (row_len + 7) / 8;
+  p.n_chunks = n_rows * p.chunks_per_row;
+  return device_status(launch_unpack(p, stream));
+}
+
+int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const cache,
+                   float* out, hipStream_t stream) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (n_filled < 0 || n_filled > layout->n_blocks) return KVQ_E_INVAL;
+  if (!cache_ok(cache) || !out || !aligned16(out)) return KVQ_E_INVAL;
+  const int sup = gpu_supported(layout);
+  if (sup != KVQ_OK) return sup;
+  DequantParams p;
+  memset(&p, 0, sizeof(p));
+  p.codes = cache.codes;
+  p.zero = cache.zero;
+  p.scale = cache.scale;
+  p.out = out;
+  p.H = layout->heads;
+  p.D = layout->head_dim;
+  p.bits = layout->bits;
+  p.R = row_bytes(layout->bits, layout->head_dim);
+  p.NB = layout->n_blocks;
+  p.n_filled = n_filled;
+  p.T_cache = offset_of(layout, layout->n_blocks);
+  p.T_out = offset_of(layout, n_filled);
+  int64_t e = 0;
+  for (int i = 0; i < layout->n_blocks; ++i) {
+    e += layout->block_tokens[i];
+    p.block_end[i] = (int32_t)e;
+  }
+  p.n_chunks = (int64_t)layout->batch * layout->heads * p.T_out * (p.D / 8);
+  return device_status(launch_dequantize(p, stream));
+}
+
+int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
+                      kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
+                      float* out, hipStream_t stream) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (block < 0 || block >= layout->n_blocks) return KVQ_E_INVAL;
+  if (!q_bf16 || !out || !aligned16(q_bf16) || !aligned16(out)) return KVQ_E_INVAL;
+  if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
+  if (!(scale == scale) || isinf(scale)) return KVQ_E_INVAL;
+  const int sup = gpu_supported(layout);
+  if (sup != KVQ_OK) return sup;
+  AttendParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q_bf16;
+  p.kcodes = k_cache.codes;
+  p.kzero = k_cache.zero;
+  p.kscale = k_cache.scale;
+  p.vcodes = v_cache.codes;
+  p.vzero = v_cache.zero;
+  p.vscale = v_cache.scale;
+  p.out = out;
+  p.T_cache = offset_of(layout, layout->n_blocks);
+  p.B = layout->batch;
+  p.H = layout->heads;
+  p.n = layout->block_tokens[block];
+  p.NB = layout->n_blocks;
+  p.R = row_bytes(layout->bits, layout->head_dim);
+  p.n_prefix = (int32_t)offset_of(layout, block + 1);
+  p.n_kblocks = block + 1;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)layout->head_dim);
+  p.scale_log2 = (float)(sc * 1.4426950408889634);
+  int64_t e = 0;
+  for (int i = 0; i < layout->n_blocks; ++i) {
+    e += layout->block_tokens[i];
+    p.block_end[i] = (int32_t)e;
+  }
+  return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+}
+
+int kvq_stream_copy(const void* src, void* dst, uint64_t n_bytes, hipStream_t stream) {
+  if (n_bytes % 16 != 0) return KVQ_E_INVAL;
+  if (n_bytes == 0) return KVQ_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return KVQ_E_INVAL;
+  return device_status(launch_stream_copy(src, dst, n_bytes, stream));
+}
+
+}  // extern "C"

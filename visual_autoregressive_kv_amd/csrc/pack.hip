@@ -1,0 +1,158 @@
+// pack.hip -- standalone bit-packing (kvq_pack) plus the test-only unpack and
+// dequantize kernels and the plain streaming copy used to measure HBM peak.
+//
+// Packing follows the cache-row layout of the fused quantizer: a row of codes is
+// an LSB-first bit stream, code d at stream bits [bits*d, bits*d + bits); eight
+// codes therefore fill exactly `bits` bytes.  One thread packs one 8-code chunk
+// (one 64-bit load of 8 code bytes); when destination rows are back to back the
+// workgroup's bytes are one contiguous span, staged in LDS and written with
+// 128-bit stores, otherwise each chunk is written bytewise in place.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWG = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint64_t pack8(uint64_t codes8, int bits, int count) {
+  const uint32_t mask = (1u << bits) - 1u;
+  uint64_t w = 0;
+  for (int j = 0; j < count; ++j) w |= (uint64_t)((codes8 >> (8 * j)) & mask) << (bits * j);
+  return w;
+}
+
+__global__ __launch_bounds__(kWG) void pack_kernel(PackParams p) {
+  __shared__ __align__(16) uint8_t stage[kWG * 8 + 32];
+  const int64_t chunk = (int64_t)blockIdx.x * kWG + threadIdx.x;
+  const bool ok = chunk < p.n_chunks;
+  const int64_t row = ok ? chunk / p.chunks_per_row : 0;
+  const int c = ok ? (int)(chunk - row * p.chunks_per_row) : 0;
+  const int count = min(8, p.row_len - 8 * c);
+  uint64_t w = 0;
+  if (ok) {
+    const uint8_t* src = p.codes + row * p.row_len + 8 * c;
+    uint64_t codes8 = 0;
+    if (count == 8 && ((reinterpret_cast<uintptr_t>(src) & 7) == 0)) {
+      codes8 = *reinterpret_cast<const uint64_t*>(src);
+    } else {
+      for (int j = 0; j < count; ++j) codes8 |= (uint64_t)src[j] << (8 * j);
+    }
+    w = pack8(codes8, p.bits, count);
+  }
+  const int nb = ok ? (p.bits * count + 7) / 8 : 0;
+  if (p.contiguous) {
+    // the workgroup's chunks map to one contiguous span of dst
+    const int64_t first = (int64_t)blockIdx.x * kWG;
+    const int64_t last = min(first + kWG, p.n_chunks);
+    uint8_t* dst = p.dst + first * p.bits;
+    const int nbytes = (int)((last - first) * p.bits);
+    const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
+    uint8_t* sp = stage + mis + (int)(chunk - first) * p.bits;
+    for (int j = 0; j < nb; ++j) sp[j] = (uint8_t)(w >> (8 * j));
+    __syncthreads();
+    const int head = min((16 - mis) & 15, nbytes);
+    const int body = (nbytes - head) >> 4;
+    const int tail = nbytes - head - (body << 4);
+    const uint8_t* s0 = stage + mis;
+    for (int k = threadIdx.x; k < body; k += kWG)
+      *reinterpret_cast<u32x4*>(dst + head + 16 * k) =
+          *reinterpret_cast<const u32x4*>(s0 + head + 16 * k);
+    if ((int)threadIdx.x < head) dst[threadIdx.x] = s0[threadIdx.x];
+    if ((int)threadIdx.x < tail) dst[head + 16 * body + threadIdx.x] = s0[head + 16 * body + threadIdx.x];
+  } else if (ok) {
+    uint8_t* dst = p.dst + row * p.dst_stride + (int64_t)c * p.bits;
+    for (int j = 0; j < nb; ++j) dst[j] = (uint8_t)(w >> (8 * j));
+  }
+}
+
+__global__ __launch_bounds__(kWG) void unpack_kernel(UnpackParams p) {
+  const int64_t chunk = (int64_t)blockIdx.x * kWG + threadIdx.x;
+  if (chunk >= p.n_chunks) return;
+  const int64_t row = chunk / p.chunks_per_row;
+  const int c = (int)(chunk - row * p.chunks_per_row);
+  const int count = min(8, p.row_len - 8 * c);
+  const int nb = (p.bits * count + 7) / 8;
+  const uint8_t* src = p.src + row * p.src_stride + (int64_t)c * p.bits;
+  uint64_t w = 0;
+  for (int j = 0; j < nb; ++j) w |= (uint64_t)src[j] << (8 * j);
+  const uint32_t mask = (1u << p.bits) - 1u;
+  uint8_t* out = p.codes + row * p.row_len + 8 * c;
+  for (int j = 0; j < count; ++j) out[j] = (uint8_t)((w >> (p.bits * j)) & mask);
+}
+
+// one thread = 8 channels of one cached token
+__global__ __launch_bounds__(kWG) void dequant_kernel(DequantParams p) {
+  const int64_t chunk = (int64_t)blockIdx.x * kWG + threadIdx.x;
+  if (chunk >= p.n_chunks) return;
+  const int cpr = p.D / 8;
+  const int64_t rowid = chunk / cpr;  // (b*H + h) * T_out + t
+  const int cg = (int)(chunk - rowid * cpr);
+  const int64_t bh = rowid / p.T_out;
+  const int64_t t = rowid - bh * p.T_out;
+  int k = 0;
+  while (k < p.n_filled - 1 && t >= p.block_end[k]) ++k;
+  const uint8_t* row = p.codes + (bh * p.T_cache + t) * p.R + (int64_t)cg * p.bits;
+  uint64_t w = 0;
+  for (int j = 0; j < p.bits; ++j) w |= (uint64_t)row[j] << (8 * j);
+  const uint32_t mask = (1u << p.bits) - 1u;
+  const int64_t so = (bh * p.NB + k) * p.D + 8 * cg;
+  float* out = p.out + rowid * p.D + 8 * cg;
+  for (int j = 0; j < 8; ++j) {
+    const float code = (float)((w >> (p.bits * j)) & mask);
+    out[j] = __builtin_fmaf(code, h2f(p.scale[so + j]), h2f(p.zero[so + j]));
+  }
+}
+
+// grid-stride 16-byte copy, 4 loads in flight per thread
+__global__ __launch_bounds__(kWG) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * kWG;
+  uint64_t i = (uint64_t)blockIdx.x * kWG + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 a = __builtin_nontemporal_load(src + i);
+    u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+    __builtin_nontemporal_store(c, dst + i + 2 * stride);
+    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+  }
+  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackParams& p, hipStream_t s) {
+  if (p.n_chunks == 0) return hipSuccess;
+  const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const UnpackParams& p, hipStream_t s) {
+  if (p.n_chunks == 0) return hipSuccess;
+  const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
+  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantParams& p, hipStream_t s) {
+  if (p.n_chunks == 0) return hipSuccess;
+  const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n, hipStream_t s) {
+  const uint64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  const unsigned grid = 256 * 16;  // 16 workgroups per CU
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(kWG), 0, s,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,337 @@
+// quant_pack.hip -- fused VAR-Q quantize + bit-pack of one decoded block (gfx950).
+//
+// VAR-Q (abstract, "groups along the same two axes"): one asymmetric min/max
+// grid per (sequence, block, head, channel) group; the block boundary is the
+// one the decode loop hands over.  One workgroup pass streams a block's K and V
+// from HBM exactly once:
+//   1. every thread loads 8-channel chunks (128-bit loads) of its rows into
+//      registers (a (tensor, b, h) tile of n_k x D values is spread over
+//      `gs` threads, `rpt` rows each);
+//   2. per-channel min/max: v_min3/v_max3 over row pairs, then an xor
+//      butterfly over the lanes holding the same channels, then across waves
+//      through LDS;
+//   3. zero = binary16 rounded down from the min, step = binary16 rounded up
+//      from fp32(max - zero)/(2^b - 1), reciprocal once per channel;
+//   4. codes from the register copy: sub, mul, clamp (v_med3), and a
+//      +2^23 add that rounds half-to-even and leaves the integer in the low
+//      mantissa bits, summed straight into the packed word with shift-adds;
+//   5. packed bytes staged in LDS (3-bit rows are 24 bytes: codes 2 and 5 of
+//      each 8 straddle bytes and a block's rows may start 8 bytes off a
+//      16-byte boundary) and written with coalesced 128-bit stores, never
+//      touching bytes outside the block's rows.
+// Tiles too large for registers (video frames) take two passes over HBM.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWG = 256;
+constexpr int kMaxRpt = 8;
+constexpr int kStageBytes = kWG * kMaxRpt * 4 + 16 * 32;
+
+template <int BITS>
+struct PackMagic {
+  // sum over the 8 codes of the exponent bits 0x4B000000 of (2^23 + code),
+  // shifted to the code's position, modulo 2^32
+  static constexpr uint32_t value() {
+    uint32_t s = 0;
+    for (int j = 0; j < 8; ++j) s += (0x4B000000u << (BITS * j));
+    return s;
+  }
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool F32>
+struct Chunk;
+template <>
+struct Chunk<false> {
+  u32x4 w;  // 8 bf16; channel 2j in the low half of word j
+};
+template <>
+struct Chunk<true> {
+  f32x4 a, b;
+};
+
+template <bool F32>
+__device__ __forceinline__ void load_chunk(Chunk<F32>& c, const void* base, int64_t elem) {
+  if constexpr (F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem);
+    c.a = __builtin_nontemporal_load(p);
+    c.b = __builtin_nontemporal_load(p + 1);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+    c.w = __builtin_nontemporal_load(p);
+  }
+}
+
+__device__ __forceinline__ uint32_t word_of(const u32x4& w, int j) {
+  return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+}
+
+// exact binary32 value of channel j
+template <bool F32>
+__device__ __forceinline__ float chan(const Chunk<F32>& c, int j) {
+  if constexpr (F32) {
+    const float v[8] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w};
+    return v[j];
+  } else {
+    uint32_t w = word_of(c.w, j >> 1);
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+}
+
+// value used only for ordering: for odd bf16 channels the raw word, whose low
+// 16 bits (the neighbouring channel) sit below the bf16 value's last bit and so
+// never change its order against another bf16 value; masked off afterwards
+template <bool F32>
+__device__ __forceinline__ float chan_order(const Chunk<F32>& c, int j) {
+  if constexpr (F32) {
+    return chan<true>(c, j);
+  } else {
+    uint32_t w = word_of(c.w, j >> 1);
+    return __uint_as_float((j & 1) ? w : (w << 16));
+  }
+}
+
+template <bool F32>
+__device__ __forceinline__ int nonfinite(const Chunk<F32>& c) {
+  int bad = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bad |= !__builtin_isfinite(chan<F32>(c, j));
+  return bad;
+}
+
+template <int D, int BITS, bool F32, bool CHECK, bool STREAM>
+__global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
+  constexpr int CPR = D / 8;  // 8-channel chunks per row
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  __shared__ __align__(16) uint8_t stage[kStageBytes];
+  __shared__ float red_mn[kWG / kWave][CPR][8];
+  __shared__ float red_mx[kWG / kWave][CPR][8];
+
+  const int tid = threadIdx.x;
+  const int gs = p.gs;
+  const int rpt = p.rpt;
+  const int slot = tid / gs;
+  const int lt = tid - slot * gs;
+  const int64_t tile = (int64_t)blockIdx.x * (kWG / gs) + slot;
+  const bool tile_ok = tile < p.n_tiles;
+  const int kv = tile_ok ? (int)(tile / p.BH) : 0;
+  const int bh = tile_ok ? (int)(tile - (int64_t)kv * p.BH) : 0;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int cg = lt % CPR;
+  const int r0 = lt / CPR;
+  const int rps = gs / CPR;           // rows covered by one sweep of the tile's threads
+  const int rows_per_pass = rps * rpt;
+  const int n = tile_ok ? p.n : 0;
+  const void* src = p.src[kv];
+  const int64_t row_stride = (int64_t)p.H * D;            // elements between tokens
+  const int64_t base = ((int64_t)b * p.n * p.H + h) * D + 8 * cg;
+  const int slot_bytes = ((gs * rpt * BITS + 16) + 15) & ~15;
+  uint8_t* my_stage = stage + slot * slot_bytes;
+
+  Chunk<F32> v[kMaxRpt];
+  float mn[8], mx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mn[j] = __uint_as_float(0x7F800000u);
+    mx[j] = __uint_as_float(0xFF800000u);
+  }
+  int bad = 0;
+
+  // ---- phase 1: load + per-thread extremes --------------------------------
+  const int n_pass = STREAM ? (n + rows_per_pass - 1) / rows_per_pass : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int row_base = pass * rows_per_pass + r0;
+    int nvalid = 0;
+    if (row_base < n) nvalid = min(rpt, (n - row_base + rps - 1) / rps);
+#pragma unroll
+    for (int i = 0; i < kMaxRpt; ++i)
+      if (i < nvalid) load_chunk<F32>(v[i], src, base + (int64_t)(row_base + i * rps) * row_stride);
+#pragma unroll
+    for (int i = 0; i < kMaxRpt; i += 2) {
+      if (i < nvalid) {
+        const int i2 = (i + 1 < nvalid) ? i + 1 : i;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float a = chan_order<F32>(v[i], j);
+          const float c = chan_order<F32>(v[i2], j);
+          mn[j] = min3f(mn[j], a, c);
+          mx[j] = max3f(mx[j], a, c);
+        }
+        if constexpr (CHECK) bad |= nonfinite<F32>(v[i]) | nonfinite<F32>(v[i2]);
+      }
+    }
+  }
+
+  // ---- phase 2: reduce across the tile's threads ---------------------------
+  const int lanes = min(gs, kWave);
+  for (int m = CPR; m < lanes; m <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
+      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
+    }
+  }
+  if (gs > kWave) {
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    if (lane < CPR) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        red_mn[wave][lane][j] = mn[j];
+        red_mx[wave][lane][j] = mx[j];
+      }
+    }
+    __syncthreads();
+    const int wpt = gs / kWave;
+    const int w0 = slot * wpt;
+    for (int w = 0; w < wpt; ++w) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mn[j] = fminf(mn[j], red_mn[w0 + w][cg][j]);
+        mx[j] = fmaxf(mx[j], red_mx[w0 + w][cg][j]);
+      }
+    }
+  }
+
+  // ---- phase 3: per-channel statistics -------------------------------------
+  float zf[8], inv[8];
+  uint16_t zb[8], sb[8];
+  int flags = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float lo = mn[j], hi = mx[j];
+    if (!F32 && (j & 1)) {
+      lo = __uint_as_float(__float_as_uint(lo) & 0xFFFF0000u);
+      hi = __uint_as_float(__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    lo = (lo == 0.0f) ? 0.0f : lo;  // a zero extreme is +0
+    hi = (hi == 0.0f) ? 0.0f : hi;
+    if constexpr (CHECK) {
+      if (!(lo >= -65504.0f) || !(hi <= 65504.0f)) flags |= KVQ_S_RANGE;
+    }
+    zb[j] = rd16(lo);
+    zf[j] = h2f(zb[j]);
+    const float r = hi - zf[j];
+    const float q = r / LEVELS;
+    sb[j] = ru16(q);
+    const float sf = h2f(sb[j]);
+    if constexpr (CHECK) {
+      if (!(sf <= 65504.0f)) flags |= KVQ_S_RANGE;
+    }
+    inv[j] = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+  }
+  if (tile_ok && r0 == 0) {
+    const int64_t so = (((int64_t)b * p.H + h) * p.NB + p.block) * D + 8 * cg;
+    u32x4 zw, sw;
+    zw.x = zb[0] | ((uint32_t)zb[1] << 16);
+    zw.y = zb[2] | ((uint32_t)zb[3] << 16);
+    zw.z = zb[4] | ((uint32_t)zb[5] << 16);
+    zw.w = zb[6] | ((uint32_t)zb[7] << 16);
+    sw.x = sb[0] | ((uint32_t)sb[1] << 16);
+    sw.y = sb[2] | ((uint32_t)sb[3] << 16);
+    sw.z = sb[4] | ((uint32_t)sb[5] << 16);
+    sw.w = sb[6] | ((uint32_t)sb[7] << 16);
+    *reinterpret_cast<u32x4*>(p.zero[kv] + so) = zw;
+    *reinterpret_cast<u32x4*>(p.scale[kv] + so) = sw;
+  }
+  if constexpr (CHECK) {
+    if (bad) flags |= KVQ_S_NONFINITE;
+    if (tile_ok && flags) atomicOr(p.status, flags);
+  }
+
+  // ---- phase 4: codes, pack, stage, store ----------------------------------
+  uint8_t* dst_tile = p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int pass_row0 = pass * rows_per_pass;
+    const int row_base = pass_row0 + r0;
+    int nvalid = 0;
+    if (row_base < n) nvalid = min(rpt, (n - row_base + rps - 1) / rps);
+    if constexpr (STREAM) {
+#pragma unroll
+      for (int i = 0; i < kMaxRpt; ++i)
+        if (i < nvalid)
+          load_chunk<F32>(v[i], src, base + (int64_t)(row_base + i * rps) * row_stride);
+    }
+    uint8_t* dst = dst_tile + (int64_t)pass_row0 * p.R;
+    const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
+#pragma unroll
+    for (int i = 0; i < kMaxRpt; ++i) {
+      if (i < nvalid) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float t = chan<F32>(v[i], j) - zf[j];
+          const float u = t * inv[j];
+          const float c = __builtin_amdgcn_fmed3f(u, 0.0f, LEVELS);
+          const float f = c + 8388608.0f;  // 2^23: rounds half-to-even into the low bits
+          acc += __float_as_uint(f) << (BITS * j);
+        }
+        acc -= PackMagic<BITS>::value();
+        const int chunk = (r0 + i * rps) * CPR + cg;  // within this pass
+        uint8_t* sp = my_stage + mis + chunk * BITS;
+        if constexpr (BITS == 4) {
+          *reinterpret_cast<uint32_t*>(sp) = acc;
+        } else {
+          sp[0] = (uint8_t)acc;
+          sp[1] = (uint8_t)(acc >> 8);
+          sp[2] = (uint8_t)(acc >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    const int rows_here = max(0, min(n - pass_row0, rows_per_pass));
+    const int nbytes = rows_here * p.R;
+    const int head = min((16 - mis) & 15, nbytes);
+    const int body = (nbytes - head) >> 4;
+    const int tail = nbytes - head - (body << 4);
+    const uint8_t* sp = my_stage + mis;
+    for (int k = lt; k < body; k += gs)
+      *reinterpret_cast<u32x4*>(dst + head + 16 * k) =
+          *reinterpret_cast<const u32x4*>(sp + head + 16 * k);
+    if (lt < head) dst[lt] = sp[lt];
+    if (lt < tail) dst[head + 16 * body + lt] = sp[head + 16 * body + lt];
+    if constexpr (STREAM) __syncthreads();
+  }
+}
+
+template <int D, int BITS, bool F32>
+hipError_t launch_t(const QuantParams& p, hipStream_t s) {
+  const int tiles_per_wg = kWG / p.gs;
+  const int64_t grid = (p.n_tiles + tiles_per_wg - 1) / tiles_per_wg;
+  const bool stream = (int64_t)(p.gs / (D / 8)) * p.rpt < p.n;
+  const bool check = p.status != nullptr;
+  dim3 g((unsigned)grid), blk(kWG);
+  if (check) {
+    if (stream)
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, true, true>), g, blk, 0, s, p);
+    else
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, true, false>), g, blk, 0, s, p);
+  } else {
+    if (stream)
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, false, true>), g, blk, 0, s, p);
+    else
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, false, false>), g, blk, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const QuantParams& p, int bits, bool f32src, hipStream_t s) {
+  if (bits == 4) return f32src ? launch_t<D, 4, true>(p, s) : launch_t<D, 4, false>(p, s);
+  return f32src ? launch_t<D, 3, true>(p, s) : launch_t<D, 3, false>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantParams& p, int head_dim, int bits, bool f32src,
+                           hipStream_t s) {
+  if (head_dim == 64) return launch_d<64>(p, bits, f32src, s);
+  return launch_d<128>(p, bits, f32src, s);
+}
+
+}  // namespace kvq

@@ -1,0 +1,241 @@
+"""Thin Python binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels of libkvq.so; torch supplies
+device memory and the current stream.  The shapes of the tensors handed in are
+checked against the layout here, because the C ABI only sees raw pointers.
+Import fails loudly when the library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "kvq.h")
+
+MAX_BLOCKS = 64
+OK, E_INVAL, E_UNSUPPORTED, E_DEVICE = 0, -1, -2, -3
+S_NONFINITE, S_RANGE = 1, 2
+F32, BF16 = 0, 1
+ERRORS = {E_INVAL: "KVQ_E_INVAL", E_UNSUPPORTED: "KVQ_E_UNSUPPORTED", E_DEVICE: "KVQ_E_DEVICE"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {ERRORS.get(code, code)}")
+        self.code = code
+
+
+class Layout(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
+        ("bits", C.c_int32), ("n_blocks", C.c_int32), ("pack_mode", C.c_int32),
+        ("block_tokens", C.c_int32 * MAX_BLOCKS),
+    ]
+
+    @property
+    def blocks(self) -> Tuple[int, ...]:
+        return tuple(int(self.block_tokens[i]) for i in range(self.n_blocks))
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.blocks))
+
+    def offset(self, block: int) -> int:
+        return int(sum(self.blocks[:block]))
+
+    @property
+    def row_bytes(self) -> int:
+        return (self.bits * self.head_dim + 7) // 8
+
+
+class Cache(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("zero", C.c_void_p), ("scale", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libkvq.so; raises if it is not built (no silent fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m visual_autoregressive_kv_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, u64 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64
+        L.kvq_version.restype = C.c_char_p
+        L.kvq_version.argtypes = []
+        L.kvq_bytes.restype = C.c_int
+        L.kvq_bytes.argtypes = [C.POINTER(Layout), i32, C.POINTER(u64), C.POINTER(u64)]
+        L.kvq_quantize_block.restype = C.c_int
+        L.kvq_quantize_block.argtypes = [C.POINTER(Layout), i32, i32, vp, vp, Cache, Cache, vp, vp]
+        L.kvq_pack.restype = C.c_int
+        L.kvq_pack.argtypes = [i32, i32, vp, i64, i32, vp, i64, vp]
+        L.kvq_unpack.restype = C.c_int
+        L.kvq_unpack.argtypes = [i32, i32, vp, i64, i64, i32, vp, vp]
+        L.kvq_dequantize.restype = C.c_int
+        L.kvq_dequantize.argtypes = [C.POINTER(Layout), i32, Cache, vp, vp]
+        L.kvq_attend_packed.restype = C.c_int
+        L.kvq_attend_packed.argtypes = [C.POINTER(Layout), i32, vp, Cache, Cache, C.c_float, vp,
+                                        vp]
+        L.kvq_stream_copy.restype = C.c_int
+        L.kvq_stream_copy.argtypes = [vp, vp, u64, vp]
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> Sequence[str]:
+    """Function names declared in include/kvq.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != OK:
+        raise KvqError(fn, rc)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a CUDA/HIP device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# layout and cache helpers
+# ---------------------------------------------------------------------------
+
+def make_layout(batch: int, heads: int, head_dim: int, bits: int, blocks: Sequence[int],
+                pack_mode: int = 0) -> Layout:
+    if len(blocks) > MAX_BLOCKS:
+        raise ValueError("too many blocks")
+    L = Layout()
+    L.batch, L.heads, L.head_dim, L.bits = batch, heads, head_dim, bits
+    L.n_blocks, L.pack_mode = len(blocks), pack_mode
+    for i, n in enumerate(blocks):
+        L.block_tokens[i] = int(n)
+    return L
+
+
+def kvq_bytes(layout: Layout, n_filled: int) -> Tuple[int, int]:
+    cb, sb = C.c_uint64(), C.c_uint64()
+    _check("kvq_bytes", lib().kvq_bytes(C.byref(layout), n_filled, C.byref(cb), C.byref(sb)))
+    return int(cb.value), int(sb.value)
+
+
+def cache_shapes(layout: Layout) -> Dict[str, Tuple[int, ...]]:
+    B, H, D, NB = layout.batch, layout.heads, layout.head_dim, layout.n_blocks
+    return {"codes": (B, H, layout.total_tokens, layout.row_bytes), "zero": (B, H, NB, D),
+            "scale": (B, H, NB, D)}
+
+
+def alloc_cache(layout: Layout, device="cuda") -> Dict[str, torch.Tensor]:
+    """Device buffers of one packed cache (sizes agree with kvq_bytes(layout, n_blocks))."""
+    s = cache_shapes(layout)
+    return {"codes": torch.zeros(s["codes"], dtype=torch.uint8, device=device),
+            "zero": torch.zeros(s["zero"], dtype=torch.float16, device=device),
+            "scale": torch.zeros(s["scale"], dtype=torch.float16, device=device)}
+
+
+def _cache(layout: Layout, c: Dict[str, torch.Tensor], name: str) -> Cache:
+    s = cache_shapes(layout)
+    return Cache(_dev(c["codes"], name + ".codes", torch.uint8, s["codes"]),
+                 _dev(c["zero"], name + ".zero", torch.float16, s["zero"]),
+                 _dev(c["scale"], name + ".scale", torch.float16, s["scale"]))
+
+
+def _block_shape(layout: Layout, block: int):
+    if not 0 <= block < layout.n_blocks:
+        raise ValueError("block out of range")
+    return (layout.batch, layout.block_tokens[block], layout.heads, layout.head_dim)
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, one function each
+# ---------------------------------------------------------------------------
+
+def kvq_quantize_block(layout: Layout, block: int, k_src: torch.Tensor, v_src: torch.Tensor,
+                       k_cache, v_cache, status: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    shp = _block_shape(layout, block)
+    if k_src.dtype != v_src.dtype:
+        raise ValueError("k_src and v_src dtypes differ")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(k_src.dtype)
+    if dt is None:
+        raise ValueError("source dtype must be float32 or bfloat16")
+    kp = _dev(k_src, "k_src", k_src.dtype, shp)
+    vp = _dev(v_src, "v_src", v_src.dtype, shp)
+    sp = None if status is None else _dev(status, "status", torch.int32, (1,))
+    _check("kvq_quantize_block",
+           lib().kvq_quantize_block(C.byref(layout), block, dt, kp, vp,
+                                    _cache(layout, k_cache, "k_cache"),
+                                    _cache(layout, v_cache, "v_cache"), sp, _stream(stream)))
+
+
+def kvq_pack(bits: int, codes: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """codes: uint8 [n_rows, row_len]; dst: uint8 [n_rows, stride >= ceil(bits*row_len/8)]."""
+    if codes.dim() != 2 or dst.dim() != 2 or codes.shape[0] != dst.shape[0]:
+        raise ValueError("codes [n_rows, row_len] and dst [n_rows, stride] expected")
+    n_rows, row_len = codes.shape
+    _check("kvq_pack", lib().kvq_pack(bits, 0, _dev(codes, "codes", torch.uint8), n_rows, row_len,
+                                      _dev(dst, "dst", torch.uint8), dst.shape[1],
+                                      _stream(stream)))
+
+
+def kvq_unpack(bits: int, src: torch.Tensor, row_len: int, codes: torch.Tensor,
+               stream=None) -> None:
+    if src.dim() != 2 or tuple(codes.shape) != (src.shape[0], row_len):
+        raise ValueError("src [n_rows, stride] and codes [n_rows, row_len] expected")
+    _check("kvq_unpack", lib().kvq_unpack(bits, 0, _dev(src, "src", torch.uint8), src.shape[1],
+                                          src.shape[0], row_len,
+                                          _dev(codes, "codes", torch.uint8), _stream(stream)))
+
+
+def kvq_dequantize(layout: Layout, n_filled: int, cache, out: torch.Tensor,
+                   stream=None) -> None:
+    T = layout.offset(n_filled)
+    shp = (layout.batch, layout.heads, T, layout.head_dim)
+    _check("kvq_dequantize",
+           lib().kvq_dequantize(C.byref(layout), n_filled, _cache(layout, cache, "cache"),
+                                _dev(out, "out", torch.float32, shp), _stream(stream)))
+
+
+def kvq_attend_packed(layout: Layout, block: int, q: torch.Tensor, k_cache, v_cache,
+                      out: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+    shp = _block_shape(layout, block)
+    _check("kvq_attend_packed",
+           lib().kvq_attend_packed(C.byref(layout), block, _dev(q, "q", torch.bfloat16, shp),
+                                   _cache(layout, k_cache, "k_cache"),
+                                   _cache(layout, v_cache, "v_cache"), float(scale),
+                                   _dev(out, "out", torch.float32, shp), _stream(stream)))
+
+
+def kvq_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _check("kvq_stream_copy", lib().kvq_stream_copy(_dev(src, "src"), _dev(dst, "dst"), n,
+                                                    _stream(stream)))
+
+
+def kvq_version() -> str:
+    return lib().kvq_version().decode()
