@@ -1,0 +1,324 @@
+"""Benchmark of the VAR-Q packed-KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one full block-by-block decode pass of the workload: for every
+scale k of the 10-scale VAR schedule and every layer, quantize + bit-pack the
+freshly decoded block's K and V into that layer's packed cache
+(kvq_quantize_block), then run block-causal attention of the block's queries
+over the packed cache (kvq_attend_packed).  Inputs (K, V, Q of every block of
+every layer, bf16, synthetic VAR-shaped data drawn on the device) and caches
+are resident in HBM before the timed region; every layer has its own buffers,
+so the 256 MB last-level cache cannot serve repeats.
+
+Printed: one JSON line.  `value` is packed-KV attention tokens/s over the whole
+step (query tokens x layers per second, quantize+pack included); per-kernel
+figures come from HIP events recorded around every launch on the launch stream
+during the timed steps; `roofline` is for the kernel with the larger share of
+the step; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "var_d20_b128_int4"
+KERNEL_SOURCES = {
+    "quant_pack": "visual_autoregressive_kv_amd/csrc/quant_pack.hip",
+    "attend": "visual_autoregressive_kv_amd/csrc/attend.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes / flops (per launch)
+# ---------------------------------------------------------------------------
+
+def quant_bytes(wl, k: int) -> int:
+    """Read the block's K and V once, write their packed rows and statistics."""
+    B, H, D, n = wl.batch, wl.heads, wl.head_dim, wl.blocks[k]
+    R = (wl.bits * D + 7) // 8
+    src = 2 if wl.src == "bf16" else 4
+    return 2 * (B * n * H * D * src + B * H * n * R + B * H * D * 4)
+
+
+def attend_bytes(wl, k: int) -> int:
+    """Packed K/V prefix + their stats once per (sequence, head), Q in, O out (fp32)."""
+    B, H, D, n = wl.batch, wl.heads, wl.head_dim, wl.blocks[k]
+    R = (wl.bits * D + 7) // 8
+    T = wl.offset(k) + n
+    return B * H * (2 * T * R + 2 * (k + 1) * D * 4 + n * D * 2 + n * D * 4)
+
+
+def attend_flops(wl, k: int) -> int:
+    B, H, D, n = wl.batch, wl.heads, wl.head_dim, wl.blocks[k]
+    T = wl.offset(k) + n
+    return 4 * B * H * n * T * D
+
+
+def source_sha(rel: str) -> str:
+    return hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle as it stands, on the host's cores: quantize + pack every block
+    and attend every block's queries for a sample of sequences of one layer.
+    Threads each take whole sequences (the oracle itself is single-threaded)."""
+    import numpy as np
+
+    import varq_inputs as vi
+    from oracle import binding as ob
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, 16))
+    # calibrate on one sequence, then size the sample to about target_s
+    def run_seqs(seqs):
+        sub = wl.with_(batch=1)
+        Lo = ob.layout_of(sub)
+        data = []
+        for b in seqs:
+            kv = [(vi.kv_block(wl, 0, "k", j, [b]), vi.kv_block(wl, 0, "v", j, [b]),
+                   vi.q_block(wl, 0, j, [b])) for j in range(len(wl.blocks))]
+            data.append(kv)
+        def work(items, out):
+            for kv in items:
+                kc, vc = ob.alloc_cache(Lo), ob.alloc_cache(Lo)
+                for j, (kb, vb, qb) in enumerate(kv):
+                    ob.quantize_block(Lo, j, kb, vb, kc, vc)
+                    ob.attend(Lo, j, qb, kc, vc)
+            out.append(len(items))
+        chunks = [data[i::threads] for i in range(threads)]
+        done = []
+        t0 = time.perf_counter()
+        ths = [threading.Thread(target=work, args=(c, done)) for c in chunks if c]
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        return time.perf_counter() - t0, len(ths)
+
+    t1, _ = run_seqs([0])
+    n_seq = int(max(1, min(wl.batch, round(target_s * threads / max(t1, 1e-3)))))
+    n_seq = max(threads, (n_seq // threads) * threads) if n_seq >= threads else n_seq
+    n_seq = min(n_seq, wl.batch)
+    secs, used = run_seqs(list(range(n_seq)))
+    tokens = n_seq * wl.total_tokens  # query tokens of one layer
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"1 of {wl.layers} layers, {n_seq} of {wl.batch} sequences, all "
+                      f"{len(wl.blocks)} scales (quantize+pack then attend each block), "
+                      f"{secs:.1f} s on {used} threads; tokens/s = query tokens x layers "
+                      f"per second, same unit as value"}
+
+
+# ---------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build's path runs on a single MI355X "
+              "(it shards across GPUs with no exchange by batch or heads, which is not "
+              "built here); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import varq_inputs as vi
+    import visual_autoregressive_kv_amd as K
+    from visual_autoregressive_kv_amd import kvq as kb
+
+    wl = vi.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = K.lib()
+    L = K.make_layout(wl.batch, wl.heads, wl.head_dim, wl.bits, wl.blocks)
+    NB = len(wl.blocks)
+    print(f"[bench] {wl.name}: {wl.layers} layers, batch {wl.batch}, {wl.heads}x{wl.head_dim}, "
+          f"INT{wl.bits}, {NB} blocks ({wl.total_tokens} tokens); drawing inputs", flush=True)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    Kin = [[vi.torch_block(wl, l, "k", j, dev, gen) for j in range(NB)] for l in range(wl.layers)]
+    Vin = [[vi.torch_block(wl, l, "v", j, dev, gen) for j in range(NB)] for l in range(wl.layers)]
+    Qin = [[vi.torch_block(wl, l, "q", j, dev, gen) for j in range(NB)] for l in range(wl.layers)]
+    Out = [[torch.empty(Qin[l][j].shape, dtype=torch.float32, device=dev) for j in range(NB)]
+           for l in range(wl.layers)]
+    kcs = [K.alloc_cache(L, dev) for _ in range(wl.layers)]
+    vcs = [K.alloc_cache(L, dev) for _ in range(wl.layers)]
+    torch.cuda.synchronize()
+
+    # HBM copy peak on this machine (context for the roofline)
+    a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        K.kvq_stream_copy(a, c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        K.kvq_stream_copy(a, c)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, c
+
+    # pre-marshalled calls: the timed loop only crosses into the library
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+    Lref = C.byref(L)
+
+    def cache(cd):
+        return kb.Cache(cd["codes"].data_ptr(), cd["zero"].data_ptr(), cd["scale"].data_ptr())
+
+    kC = [cache(x) for x in kcs]
+    vC = [cache(x) for x in vcs]
+    qargs, aargs = [], []
+    for j in range(NB):
+        for l in range(wl.layers):
+            # shapes are fixed by construction; check them once here through the binding
+            assert tuple(Kin[l][j].shape) == (wl.batch, wl.blocks[j], wl.heads, wl.head_dim)
+            qargs.append((Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
+                          kC[l], vC[l], None, sh))
+            aargs.append((Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
+                          Out[l][j].data_ptr(), sh))
+    qfn, afn = lib.kvq_quantize_block, lib.kvq_attend_packed
+    # one checked call through the binding before the raw loop
+    K.kvq_quantize_block(L, 0, Kin[0][0], Vin[0][0], kcs[0], vcs[0])
+    K.kvq_attend_packed(L, 0, Qin[0][0], kcs[0], vcs[0], Out[0][0])
+
+    def step(events=None):
+        for i in range(len(qargs)):
+            if events is not None:
+                events[4 * i].record(stream)
+            rc = qfn(*qargs[i])
+            if events is not None:
+                events[4 * i + 1].record(stream)
+                events[4 * i + 2].record(stream)
+            rc |= afn(*aargs[i])
+            if events is not None:
+                events[4 * i + 3].record(stream)
+            if rc:
+                raise RuntimeError(f"kvq launch failed (rc={rc}) at call {i}")
+
+    for w in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", flush=True)
+
+    n_calls = len(qargs)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * n_calls)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    q_ms = sum(evs[s][4 * i].elapsed_time(evs[s][4 * i + 1])
+               for s in range(args.steps) for i in range(n_calls))
+    a_ms = sum(evs[s][4 * i + 2].elapsed_time(evs[s][4 * i + 3])
+               for s in range(args.steps) for i in range(n_calls))
+    per_layer = lambda f: sum(f(wl, j) for j in range(NB)) * wl.layers  # noqa: E731
+    qb = per_layer(quant_bytes) * args.steps
+    ab = per_layer(attend_bytes) * args.steps
+    af = per_layer(attend_flops) * args.steps
+    q_gbps = qb / (q_ms * 1e-3) / 1e9
+    a_gbps = ab / (a_ms * 1e-3) / 1e9
+    a_tflops = af / (a_ms * 1e-3) / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = wl.batch * wl.total_tokens * wl.layers  # query tokens x layers per step
+    value = tokens * args.steps / wall
+
+    dominant = "attend" if a_ms >= q_ms else "quant_pack"
+    launches = n_calls * args.steps
+    if dominant == "attend":
+        avg_bytes, avg_ms = ab / launches, a_ms / launches
+    else:
+        avg_bytes, avg_ms = qb / launches, q_ms / launches
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dominant, wl.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": dominant,
+                "avg_launch_us": round(avg_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": round(avg_bytes)}
+    out = {
+        "metric": "packed-KV attention tokens/s + quantize/pack GB/s, % of HBM peak (1 GPU)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "bits": wl.bits,
+                   "schedule": list(wl.blocks), "tokens_per_seq": wl.total_tokens,
+                   "parallelism": "none (1 GPU)"},
+        "quant_pack_GBps": round(q_gbps, 1),
+        "quant_pack_pct_hbm_peak": round(100 * q_gbps / HBM_PEAK_GBPS, 2),
+        "attend_GBps": round(a_gbps, 1),
+        "attend_pct_hbm_peak": round(100 * a_gbps / HBM_PEAK_GBPS, 2),
+        "attend_TFLOPs": round(a_tflops, 2),
+        "attend_pct_bf16_mfma_peak": round(100 * a_tflops / BF16_PEAK_TFLOPS, 2),
+        "attend_tokens_per_s_kernel": round(tokens * args.steps / (a_ms * 1e-3), 1),
+        "quant_ms_per_step": round(q_ms / args.steps, 4),
+        "attend_ms_per_step": round(a_ms / args.steps, 4),
+        "copy_peak_GBps": round(copy_gbps, 1),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
