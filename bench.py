@@ -269,6 +269,17 @@ def main():
                for s in range(args.steps) for i in range(n_calls))
     a_ms = sum(evs[s][4 * i + 2].elapsed_time(evs[s][4 * i + 3])
                for s in range(args.steps) for i in range(n_calls))
+    # per-block average kernel times (calls are ordered block-major, layer-minor)
+    def per_block(off):
+        us = []
+        for j in range(NB):
+            tot = sum(evs[s][4 * (j * wl.layers + l) + off].elapsed_time(
+                evs[s][4 * (j * wl.layers + l) + off + 1])
+                for s in range(args.steps) for l in range(wl.layers))
+            us.append(round(1e3 * tot / (args.steps * wl.layers), 2))
+        return us
+
+    q_block_us, a_block_us = per_block(0), per_block(2)
     per_layer = lambda f: sum(f(wl, j) for j in range(NB)) * wl.layers  # noqa: E731
     qb = per_layer(quant_bytes) * args.steps
     ab = per_layer(attend_bytes) * args.steps
@@ -312,6 +323,7 @@ def main():
         "quant_ms_per_step": round(q_ms / args.steps, 4),
         "attend_ms_per_step": round(a_ms / args.steps, 4),
         "copy_peak_GBps": round(copy_gbps, 1),
+        "per_block_us": {"quant_pack": q_block_us, "attend": a_block_us},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

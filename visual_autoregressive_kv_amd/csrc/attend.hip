@@ -3,22 +3,36 @@
 // Block-by-block decoding (VAR-Q abstract): the n_k queries of block k attend
 // to every cached token of blocks 0..k.  One workgroup owns up to 256 queries of
 // one (sequence, head); its waves own 32 queries each.  The packed prefix is
-// streamed once per workgroup in tiles of 32 keys:
-//   - the workgroup unpacks a tile's K and V codes and dequantizes them in
-//     registers, k_hat = fma(code, s, z) with the (block, channel) statistics;
-//     k_hat is split into a truncated bf16 high part and a bf16 remainder so
-//     the two bf16 products reproduce it to ~2^-16; v_hat is rounded to fp16;
-//     the results go to LDS (V transposed);
-//   - each wave computes S^T = K_hat Q^T with v_mfma_f32_32x32x16_bf16 (hi and lo
-//     accumulate into one fp32 tile), so every lane holds 16 keys of a single
-//     query and the row maximum is a per-lane reduction plus one exchange;
-//   - online softmax in the log2 domain; the running maximum is only moved when
-//     a tile raises it by more than 2^8 (probabilities then stay <= 256, safe
-//     in fp16), which skips the accumulator rescale on almost every tile;
+// streamed once per workgroup in tiles of 32 keys, software-pipelined:
+//   iteration j:  issue the buffer loads of tile j+1's packed codes,
+//                 compute tile j from LDS,
+//                 dequantize tile j+1 into the other LDS buffer,
+//                 one barrier.
+//   Dequantization (shared by the workgroup's waves through LDS):
+//   - every thread owns fixed items (one key x 8 channels of K or of V) and
+//     keeps the binary16 (block, channel) statistics of its key's current
+//     block in registers, refreshed from LDS only when the key crosses into the
+//     next block;
+//   - k_hat = fma(code, s, z) in fp32 straight from the binary16 statistics
+//     (v_fma_mix_f32; INT4 codes spread to bytes and converted with
+//     v_cvt_f32_ubyteN); k_hat is split into a truncated bf16 high part and a
+//     bf16 remainder, so two bf16 products reproduce it to ~2^-16;
+//   - v_hat is rounded to fp16; lanes holding neighbouring keys swap halves
+//     (DPP) so each writes dwords of (key 2m, key 2m+1) pairs into V^T, whose
+//     odd dword row stride spreads them over the LDS banks.
+//   Compute (per wave, 32 queries):
+//   - S^T = K_hat Q^T with v_mfma_f32_32x32x16_bf16 (hi and lo accumulate into
+//     one fp32 tile; the next k-step's operands are read from LDS while the
+//     current MFMAs run): every lane holds 16 keys of one query, so the row
+//     maximum is a per-lane reduction plus one v_permlane32_swap;
+//   - online softmax in the log2 domain, p = exp2(fma(s, c, -m c)); the running
+//     maximum only moves when a tile raises it by more than 2^8 (p then stays
+//     <= 256, safe in fp16), which skips the accumulator rescale on almost every
+//     tile; masking only on the last, partial tile;
 //   - P (fp16, packed round-toward-zero) feeds O^T += V_hat^T P^T with
 //     v_mfma_f32_32x32x16_f16 straight from registers: the 16 keys a lane holds
-//     are exactly the 8+8 contraction slots its lane group supplies, so only
-//     V's LDS reads follow that key order.
+//     are exactly the contraction slots its lane group supplies; the softmax
+//     denominator sums the same rounded P with v_dot2_f32_f16.
 // Output is fp32 (bf16 output rounding alone would exceed the 2e-3 bound).
 #include "kvq_internal.h"
 
@@ -27,45 +41,101 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int KT = 32;       // keys per tile
-constexpr int KPAD = 8;      // LDS row padding (elements)
+constexpr int KT = 32;                  // keys per tile
+constexpr int KPAD = 8;                 // K tile row padding (elements)
+constexpr int VROW = KT / 2 + 1;        // V^T row stride in dwords (odd)
 constexpr int kMaxWaves = 8;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr float kRescaleLog2 = 8.0f;    // lazy-rescale slack, log2 units
+constexpr int kStatsLdsHalves = 16384;  // 32 KB of binary16 statistics
 
+// byte n of a 32-bit word to fp32 (one instruction)
+template <int N>
+__device__ __forceinline__ float ubyte_f32(uint32_t w) {
+  float r;
+  if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(w));
+  if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(w));
+  if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(w));
+  if constexpr (N == 3) asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// two fp32 -> packed bf16 / fp16 pair, round to nearest even (low half = a)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// max / sum of a value and its copy 32 lanes away (lane ^ 32)
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// value of the neighbouring lane (lane ^ 1)
+__device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF,
+                                            false);
+}
+
+// the 8 codes of one packed chunk as fp32
 template <int BITS>
-__device__ __forceinline__ uint32_t load_code_bits(const uint8_t* row, int cg) {
+__device__ __forceinline__ void codes_f32(uint32_t w, float c[8]) {
   if constexpr (BITS == 4) {
-    return *reinterpret_cast<const uint32_t*>(row + 4 * cg);
+    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+    c[0] = ubyte_f32<0>(lo);
+    c[1] = ubyte_f32<0>(hi);
+    c[2] = ubyte_f32<1>(lo);
+    c[3] = ubyte_f32<1>(hi);
+    c[4] = ubyte_f32<2>(lo);
+    c[5] = ubyte_f32<2>(hi);
+    c[6] = ubyte_f32<3>(lo);
+    c[7] = ubyte_f32<3>(hi);
   } else {
-    const int byte = 3 * cg;
-    const int w = byte & ~3;
-    const int shift = (byte & 3) * 8;
-    uint64_t v = *reinterpret_cast<const uint32_t*>(row + w);
-    if (shift > 8) v |= (uint64_t)(*reinterpret_cast<const uint32_t*>(row + w + 4)) << 32;
-    return (uint32_t)(v >> shift) & 0xFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = (float)((w >> (BITS * j)) & ((1u << BITS) - 1u));
   }
 }
 
-template <int D, int BITS>
-__global__ __launch_bounds__(kMaxWaves * kWave) void attend_kernel(AttendParams p) {
+// raw buffer view of one (b, h)'s packed prefix: loads past `bytes` return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prefix_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes,
+                                           0x00020000 /* 32-bit data format */);
+}
+
+template <int D, int BITS, int NW>
+__global__ __launch_bounds__(NW * kWave) void attend_kernel(AttendParams p) {
   constexpr int CPR = D / 8;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  constexpr int KS = D / 16;  // k-steps of the QK^T contraction
-  constexpr int MT = D / 32;  // 32-row tiles of O^T
-  __shared__ __align__(16) __bf16 k_hi[KT][D + KPAD];
-  __shared__ __align__(16) __bf16 k_lo[KT][D + KPAD];
-  __shared__ __align__(16) _Float16 v_t[D][KT + KPAD];
+  constexpr int KS = D / 16;              // k-steps of the QK^T contraction
+  constexpr int MT = D / 32;              // 32-row tiles of O^T
+  constexpr int NT = NW * kWave;          // threads
+  constexpr int ITEMS = KT * CPR;         // (key, chunk) items per tensor per tile
+  constexpr int MAXI = 2 * ITEMS / NT;    // items per thread per tile
+  static_assert(2 * ITEMS % NT == 0 && ITEMS % kWave == 0, "items must split evenly");
+  __shared__ __align__(16) __bf16 k_hi[2][KT][D + KPAD];
+  __shared__ __align__(16) __bf16 k_lo[2][KT][D + KPAD];
+  __shared__ __align__(16) uint32_t v_t[2][D][VROW];  // fp16 pairs (keys 2m, 2m+1)
+  extern __shared__ __align__(16) _Float16 st[];     // [blk][tensor][z|s][D] when it fits
   __shared__ int blk_end[KVQ_MAX_BLOCKS];
 
   const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int g = lane >> 5;    // lane group: which 8 of each 16 contraction slots
@@ -74,15 +144,67 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void attend_kernel(AttendParams 
   const int qt = blockIdx.x - bh * p.q_tiles;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
-  const int q = qt * (nthreads / kWave) * 32 + wave * 32 + col;
+  const int q = qt * NW * 32 + wave * 32 + col;
   const bool q_ok = q < p.n;
+  const bool wave_live = qt * NW * 32 + wave * 32 < p.n;
+  const int nkb = p.n_kblocks;
+  const bool stats_lds = p.stats_in_lds != 0;
+  const int64_t stat_base = (int64_t)bh * p.NB * D;
+  const int n_prefix = p.n_prefix;
+  const int n_tiles = (n_prefix + KT - 1) / KT;
 
-  for (int i = tid; i < p.n_kblocks; i += nthreads) blk_end[i] = p.block_end[i];
+  // ---- item slots: (tensor, key, chunk), fixed for every tile ----------------
+  // K items: key = rem / CPR (a row chunk); V items: key = rem % KT, so
+  // neighbouring lanes hold neighbouring keys and can pair them.
+  const __amdgpu_buffer_rsrc_t rk =
+      prefix_rsrc(p.kcodes + (int64_t)bh * p.T_cache * p.R, n_prefix * p.R);
+  const __amdgpu_buffer_rsrc_t rv =
+      prefix_rsrc(p.vcodes + (int64_t)bh * p.T_cache * p.R, n_prefix * p.R);
+  int s_tensor[MAXI], s_key[MAXI], s_cg[MAXI], s_voff[MAXI], s_shift[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int it = tid + i * NT;
+    s_tensor[i] = __builtin_amdgcn_readfirstlane((wave * kWave + i * NT) / ITEMS);
+    const int rem = it - s_tensor[i] * ITEMS;
+    s_key[i] = s_tensor[i] == 0 ? rem / CPR : rem % KT;
+    s_cg[i] = s_tensor[i] == 0 ? rem % CPR : rem / KT;
+    const int byte = BITS * s_cg[i];  // chunk cg starts at byte BITS*cg of a row
+    s_voff[i] = s_key[i] * p.R + (byte & ~3);
+    s_shift[i] = (byte & 3) * 8;
+  }
 
-  // Q^T operand: 8 bf16 per k-step, kept in registers for the whole prefix
+  uint32_t pre[MAXI], pre2[MAXI];  // prefetched packed bits of the next tile
+  auto issue_loads = [&](int j) {
+    const int soff = j * KT * p.R;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const __amdgpu_buffer_rsrc_t r = s_tensor[i] == 0 ? rk : rv;
+      pre[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i], soff, 0);
+      if constexpr (BITS != 4)
+        pre2[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i] + 4, soff, 0);
+    }
+  };
+  issue_loads(0);
+
+  // ---- block ends and statistics to LDS, Q operand to registers -------------
+  for (int i = tid; i < nkb; i += NT) blk_end[i] = p.block_end[i];
+  if (stats_lds) {  // 8 binary16 values per copy
+    for (int i = tid; i < nkb * 2 * CPR; i += NT) {
+      const int blk = i / (2 * CPR);
+      const int rem = i - blk * 2 * CPR;
+      const int tensor = rem / CPR;
+      const int cg = rem - tensor * CPR;
+      const int64_t gi = stat_base + (int64_t)blk * D + 8 * cg;
+      _Float16* row = st + ((blk * 2 + tensor) * 2) * D + 8 * cg;
+      *reinterpret_cast<u32x4*>(row) =
+          *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kzero : p.vzero) + gi);
+      *reinterpret_cast<u32x4*>(row + D) =
+          *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kscale : p.vscale) + gi);
+    }
+  }
   bf16x8 qop[KS];
   {
-    const uint16_t* qrow = p.q + (((int64_t)b * p.n + q) * p.H + h) * D + 8 * g;
+    const uint16_t* qrow = p.q + (((int64_t)b * p.n + (q_ok ? q : 0)) * p.H + h) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
@@ -90,126 +212,193 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void attend_kernel(AttendParams 
       qop[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  __syncthreads();  // blk_end and statistics visible
+
+  // binary16 statistics (8 channels of z and s) of one block for one tensor
+  auto load_stats = [&](int blk, int tensor, int cg, f16x8& z, f16x8& s) {
+    if (stats_lds) {
+      const _Float16* zr = st + ((blk * 2 + tensor) * 2) * D + 8 * cg;
+      z = *reinterpret_cast<const f16x8*>(zr);
+      s = *reinterpret_cast<const f16x8*>(zr + D);
+    } else {
+      const int64_t so = stat_base + (int64_t)blk * D + 8 * cg;
+      z = *reinterpret_cast<const f16x8*>((tensor == 0 ? p.kzero : p.vzero) + so);
+      s = *reinterpret_cast<const f16x8*>((tensor == 0 ? p.kscale : p.vscale) + so);
+    }
+  };
+
+  // per-slot cache of the current block's statistics
+  int s_blk[MAXI], s_next[MAXI];
+  f16x8 s_z[MAXI], s_s[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    s_blk[i] = 0;
+    s_next[i] = blk_end[0];
+    load_stats(0, s_tensor[i], s_cg[i], s_z[i], s_s[i]);
+  }
+
+  auto dequant = [&](int j, int buf) {
+    const int t0 = j * KT;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int t = t0 + s_key[i];
+      const int cg = s_cg[i];
+      if (t < n_prefix && t >= s_next[i]) {  // crossed into a later block
+        do {
+          ++s_blk[i];
+          s_next[i] = blk_end[s_blk[i]];
+        } while (t >= s_next[i]);
+        load_stats(s_blk[i], s_tensor[i], cg, s_z[i], s_s[i]);
+      }
+      uint32_t w;
+      if constexpr (BITS == 4) {
+        w = pre[i];
+      } else {
+        const uint64_t v = (uint64_t)pre[i] | ((uint64_t)pre2[i] << 32);
+        w = (uint32_t)(v >> s_shift[i]);
+      }
+      float cf[8], x[8];
+      codes_f32<BITS>(w, cf);
+      const bool live = t < n_prefix;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        x[c] = live ? __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]) : 0.0f;
+      if (s_tensor[i] == 0) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+          const uint32_t u0 = __float_as_uint(x[c]);
+          const uint32_t u1 = __float_as_uint(x[c + 1]);
+          hi[c >> 1] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // high halves
+          lo[c >> 1] = pk_bf16(x[c] - __uint_as_float(u0 & 0xFFFF0000u),
+                               x[c + 1] - __uint_as_float(u1 & 0xFFFF0000u));
+        }
+        *reinterpret_cast<u32x4*>(&k_hi[buf][s_key[i]][8 * cg]) = hi;
+        *reinterpret_cast<u32x4*>(&k_lo[buf][s_key[i]][8 * cg]) = lo;
+      } else {
+        // channel pairs of this key as fp16; the even-key lane writes channels
+        // 0-3 and the odd-key lane channels 4-7, each as (even, odd) key pairs
+        const uint32_t h01 = pk_f16(x[0], x[1]), h23 = pk_f16(x[2], x[3]);
+        const uint32_t h45 = pk_f16(x[4], x[5]), h67 = pk_f16(x[6], x[7]);
+        const bool odd = s_key[i] & 1;
+        // each lane sends the half its neighbour writes: the even key's
+        // channels 4-7, the odd key's channels 0-3
+        const uint32_t ra = swap_adjacent(odd ? h01 : h45);
+        const uint32_t rb = swap_adjacent(odd ? h23 : h67);
+        const uint32_t lo_e = odd ? ra : h01;  // even key, first channel pair
+        const uint32_t hi_e = odd ? rb : h23;  // even key, second channel pair
+        const uint32_t lo_o = odd ? h45 : ra;  // odd key, first channel pair
+        const uint32_t hi_o = odd ? h67 : rb;  // odd key, second channel pair
+        const int d0 = 8 * cg + (odd ? 4 : 0);
+        uint32_t* vrow = &v_t[buf][d0][s_key[i] >> 1];
+        vrow[0 * VROW] = __builtin_amdgcn_perm(lo_o, lo_e, 0x05040100u);  // channel d0
+        vrow[1 * VROW] = __builtin_amdgcn_perm(lo_o, lo_e, 0x07060302u);  // d0 + 1
+        vrow[2 * VROW] = __builtin_amdgcn_perm(hi_o, hi_e, 0x05040100u);  // d0 + 2
+        vrow[3 * VROW] = __builtin_amdgcn_perm(hi_o, hi_e, 0x07060302u);  // d0 + 3
+      }
+    }
+  };
 
   f32x16 o[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
+  for (int i = 0; i < MT; ++i) o[i] = f32x16{};
+  const float c = p.scale_log2;
+  const float slack = kRescaleLog2 / c;  // in raw score units
   float m_run = -__builtin_inff();
+  float negmc = 0.0f;  // -m_run * c
   float l_run = 0.0f;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  const uint8_t* kc = p.kcodes + (int64_t)bh * p.T_cache * p.R;
-  const uint8_t* vc = p.vcodes + (int64_t)bh * p.T_cache * p.R;
-  const int64_t stat_base = (int64_t)bh * p.NB * D;
+  dequant(0, 0);
+  __syncthreads();
 
-  for (int t0 = 0; t0 < p.n_prefix; t0 += KT) {
-    __syncthreads();  // previous tile consumed (and blk_end visible)
-    // ---- unpack + dequantize one tile of K and V into LDS ----------------
-    for (int c = tid; c < 2 * KT * CPR; c += nthreads) {
-      const int tensor = c / (KT * CPR);
-      const int rem = c - tensor * (KT * CPR);
-      const int key = rem / CPR;
-      const int cg = rem - key * CPR;
-      const int t = t0 + key;
-      float x[8];
-      if (t < p.n_prefix) {
-        int blk = 0;
-        while (blk < p.n_kblocks - 1 && t >= blk_end[blk]) ++blk;
-        const uint8_t* row = (tensor == 0 ? kc : vc) + (int64_t)t * p.R;
-        const uint32_t bits = load_code_bits<BITS>(row, cg);
-        const int64_t so = stat_base + (int64_t)blk * D + 8 * cg;
-        const u32x4 zw = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kzero : p.vzero) + so);
-        const u32x4 sw = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kscale : p.vscale) + so);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int t0 = j * KT;
+    const int buf = j & 1;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) issue_loads(j + 1);
+
+    if (wave_live) {
+      // ---- S^T = K_hat Q^T -------------------------------------------------
+      f32x16 s = f32x16{};
+      bf16x8 ah[2], al[2];  // operands of the current and the next k-step
+      ah[0] = *reinterpret_cast<const bf16x8*>(&k_hi[buf][col][8 * g]);
+      al[0] = *reinterpret_cast<const bf16x8*>(&k_lo[buf][col][8 * g]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t zj = (j & 1) ? (zw[j >> 1] >> 16) : (zw[j >> 1] & 0xFFFFu);
-          const uint32_t sj = (j & 1) ? (sw[j >> 1] >> 16) : (sw[j >> 1] & 0xFFFFu);
-          const float code = (float)((bits >> (BITS * j)) & MASK);
-          x[j] = __builtin_fmaf(code, h2f((uint16_t)sj), h2f((uint16_t)zj));
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          ah[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(&k_hi[buf][col][16 * (ks + 1) + 8 * g]);
+          al[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(&k_lo[buf][col][16 * (ks + 1) + 8 * g]);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[ks & 1], qop[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[ks & 1], qop[ks], s, 0, 0, 0);
       }
-      if (tensor == 0) {
-        u32x4 hi, lo;
+      // keep the operand reads ahead of the MFMAs that consume them (the
+      // register budget of 4 waves per SIMD otherwise serializes them)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+      // ---- online softmax (log2 domain) -----------------------------------
+      if (t0 + KT > n_prefix) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const uint32_t u0 = __float_as_uint(x[j]) & 0xFFFF0000u;
-          const uint32_t u1 = __float_as_uint(x[j + 1]) & 0xFFFF0000u;
-          const float r0 = x[j] - __uint_as_float(u0);
-          const float r1 = x[j + 1] - __uint_as_float(u1);
-          hi[j >> 1] = (u0 >> 16) | u1;
-          const __bf16 l0 = (__bf16)r0;
-          const __bf16 l1 = (__bf16)r1;
-          lo[j >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        for (int r = 0; r < 16; ++r) {
+          const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+          if (t0 + key >= n_prefix) s[r] = -__builtin_inff();
         }
-        *reinterpret_cast<u32x4*>(&k_hi[key][8 * cg]) = hi;
-        *reinterpret_cast<u32x4*>(&k_lo[key][8 * cg]) = lo;
-      } else {
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v_t[8 * cg + j][key] = (_Float16)x[j];
+      for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+      mx = fmaxf(mx, s[15]);
+      mx = max_xor32(mx);
+      const bool raise = mx > m_run + slack;
+      if (__any(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) o[i] *= alpha;
+        m_run = m_new;
+        negmc = -m_new * c;
+      }
+      f16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, negmc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, negmc));
+        const f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+        l_run = __builtin_amdgcn_fdot2(hp, ones, l_run, false);
+        pb[r >> 3][(r & 7)] = hp[0];
+        pb[r >> 3][(r & 7) + 1] = hp[1];
+      }
+
+      // ---- O^T += V_hat^T P^T ------------------------------------------------
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const uint32_t* vr = &v_t[buf][32 * i + col][0];
+          u32x4 aw;
+          aw[0] = vr[8 * kk + 2 * g];
+          aw[1] = vr[8 * kk + 2 * g + 1];
+          aw[2] = vr[8 * kk + 4 + 2 * g];
+          aw[3] = vr[8 * kk + 4 + 2 * g + 1];
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, aw), pb[kk],
+                                                         o[i], 0, 0, 0);
+        }
       }
     }
+
+    if (has_next) dequant(j + 1, buf ^ 1);
     __syncthreads();
-
-    // ---- S^T = K_hat Q^T ---------------------------------------------------
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&k_hi[col][16 * ks + 8 * g]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&k_lo[col][16 * ks + 8 * g]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qop[ks], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qop[ks], s, 0, 0, 0);
-    }
-
-    // ---- online softmax (log2 domain) -------------------------------------
-    float mt = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      const float v = (t0 + key < p.n_prefix) ? s[r] * p.scale_log2 : -__builtin_inff();
-      s[r] = v;
-      mt = fmaxf(mt, v);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
-    if (__any(m_new != m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < MT; ++i) o[i] *= alpha;
-      m_run = m_new;
-    }
-    f16x8 pb[2];
-    float lsum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s[r] - m_run);
-      const float p1 = __builtin_amdgcn_exp2f(s[r + 1] - m_run);
-      lsum += p0 + p1;
-      const f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-      pb[r >> 3][(r & 7)] = hp[0];
-      pb[r >> 3][(r & 7) + 1] = hp[1];
-    }
-    l_run += lsum;
-
-    // ---- O^T += V_hat^T P^T --------------------------------------------------
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int d = 32 * i + col;
-        const f16x4 a0 = *reinterpret_cast<const f16x4*>(&v_t[d][16 * kk + 4 * g]);
-        const f16x4 a1 = *reinterpret_cast<const f16x4*>(&v_t[d][16 * kk + 8 + 4 * g]);
-        const f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kk], o[i], 0, 0, 0);
-      }
-    }
   }
 
   // ---- normalize and store (fp32) ----------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_xor32(l_run);
   const float inv_l = 1.0f / l_tot;
   if (q_ok) {
     float* orow = p.out + (((int64_t)b * p.n + q) * p.H + h) * D;
@@ -228,15 +417,27 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void attend_kernel(AttendParams 
   }
 }
 
+template <int D, int BITS, int NW>
+hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
+  AttendParams a = p;
+  a.q_tiles = (p.n + NW * 32 - 1) / (NW * 32);
+  const int stats_halves = p.n_kblocks * 4 * D;
+  a.stats_in_lds = stats_halves <= kStatsLdsHalves;
+  const size_t dyn = a.stats_in_lds ? (size_t)stats_halves * sizeof(_Float16) : 0;
+  const int64_t grid = (int64_t)p.B * p.H * a.q_tiles;
+  hipLaunchKernelGGL((attend_kernel<D, BITS, NW>), dim3((unsigned)grid), dim3(NW * kWave), dyn,
+                     s, a);
+  return hipGetLastError();
+}
+
+// waves per workgroup: enough 32-query waves for the block, rounded to 1/2/4/8
 template <int D, int BITS>
 hipError_t launch_t(const AttendParams& p, hipStream_t s) {
-  const int rows = min(p.n, kMaxWaves * 32);
-  const int waves = (rows + 31) / 32;
-  AttendParams a = p;
-  a.q_tiles = (p.n + waves * 32 - 1) / (waves * 32);
-  const int64_t grid = (int64_t)p.B * p.H * a.q_tiles;
-  hipLaunchKernelGGL((attend_kernel<D, BITS>), dim3((unsigned)grid), dim3(waves * kWave), 0, s, a);
-  return hipGetLastError();
+  const int waves = (min(p.n, kMaxWaves * 32) + 31) / 32;
+  if (waves <= 1) return launch_nw<D, BITS, 1>(p, s);
+  if (waves <= 2) return launch_nw<D, BITS, 2>(p, s);
+  if (waves <= 4) return launch_nw<D, BITS, 4>(p, s);
+  return launch_nw<D, BITS, 8>(p, s);
 }
 
 }  // namespace

@@ -39,6 +39,10 @@ int validate_layout(const kvq_layout* L) {
 int gpu_supported(const kvq_layout* L) {
   if (L->bits != 3 && L->bits != 4) return KVQ_E_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return KVQ_E_UNSUPPORTED;
+  // one (b, h)'s rows are addressed with 32-bit buffer offsets
+  int64_t T = 0;
+  for (int i = 0; i < L->n_blocks; ++i) T += L->block_tokens[i];
+  if (T * row_bytes(L->bits, L->head_dim) > INT32_MAX) return KVQ_E_UNSUPPORTED;
   return KVQ_OK;
 }
 
