@@ -13,8 +13,8 @@ so the 256 MB last-level cache cannot serve repeats.
 
 Printed: one JSON line.  `value` is packed-KV attention tokens/s over the whole
 step (query tokens x layers per second, quantize+pack included); per-kernel
-figures come from HIP events recorded around every launch on the launch stream
-during the timed steps; `roofline` is for the kernel with the larger share of
+figures come from HIP events recorded at every launch boundary on the launch
+stream during the timed steps; `roofline` is for the kernel with the larger share of
 the step; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
 same workload on the host's cores.
 """
@@ -236,17 +236,18 @@ def main():
     K.kvq_quantize_block(L, 0, Kin[0][0], Vin[0][0], kcs[0], vcs[0])
     K.kvq_attend_packed(L, 0, Qin[0][0], kcs[0], vcs[0], Out[0][0])
 
+    # One event per launch boundary: ev[2i] before quantize i, ev[2i+1] between
+    # quantize i and attend i, ev[2i+2] after attend i (also before quantize i+1).
     def step(events=None):
+        if events is not None:
+            events[0].record(stream)
         for i in range(len(qargs)):
-            if events is not None:
-                events[4 * i].record(stream)
             rc = qfn(*qargs[i])
             if events is not None:
-                events[4 * i + 1].record(stream)
-                events[4 * i + 2].record(stream)
+                events[2 * i + 1].record(stream)
             rc |= afn(*aargs[i])
             if events is not None:
-                events[4 * i + 3].record(stream)
+                events[2 * i + 2].record(stream)
             if rc:
                 raise RuntimeError(f"kvq launch failed (rc={rc}) at call {i}")
 
@@ -256,7 +257,7 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", flush=True)
 
     n_calls = len(qargs)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * n_calls)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -265,21 +266,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    q_ms = sum(evs[s][4 * i].elapsed_time(evs[s][4 * i + 1])
-               for s in range(args.steps) for i in range(n_calls))
-    a_ms = sum(evs[s][4 * i + 2].elapsed_time(evs[s][4 * i + 3])
-               for s in range(args.steps) for i in range(n_calls))
+    def span(s, i, off):  # off 0: quantize i, off 1: attend i
+        return evs[s][2 * i + off].elapsed_time(evs[s][2 * i + off + 1])
+
+    q_ms = sum(span(s, i, 0) for s in range(args.steps) for i in range(n_calls))
+    a_ms = sum(span(s, i, 1) for s in range(args.steps) for i in range(n_calls))
+
     # per-block average kernel times (calls are ordered block-major, layer-minor)
     def per_block(off):
         us = []
         for j in range(NB):
-            tot = sum(evs[s][4 * (j * wl.layers + l) + off].elapsed_time(
-                evs[s][4 * (j * wl.layers + l) + off + 1])
-                for s in range(args.steps) for l in range(wl.layers))
+            tot = sum(span(s, j * wl.layers + l, off)
+                      for s in range(args.steps) for l in range(wl.layers))
             us.append(round(1e3 * tot / (args.steps * wl.layers), 2))
         return us
 
-    q_block_us, a_block_us = per_block(0), per_block(2)
+    q_block_us, a_block_us = per_block(0), per_block(1)
     per_layer = lambda f: sum(f(wl, j) for j in range(NB)) * wl.layers  # noqa: E731
     qb = per_layer(quant_bytes) * args.steps
     ab = per_layer(attend_bytes) * args.steps

@@ -133,3 +133,19 @@ def test_reads_only_the_prefix(oracle):
         c["scale"][:, :, 7:] = float("inf")
     b = gpu_attend(Lg, 6, q, kg, vg)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("blocks", [(2,) * 16, (1,) * 40 + (3,), (5, 1, 30, 31, 64)])
+def test_many_short_blocks(oracle, head_dim, blocks):
+    """Short blocks whose statistics do or do not fit the per-wave LDS staging of
+    the short-block kernel (16 vs 41 blocks), and 30/31/64-query blocks."""
+    wl = vi.Workload("short", 1, 2, 5, head_dim, 4 if head_dim == 64 else 3, blocks, "bf16",
+                     rope=False, seed=5)
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)
+    for block in sorted({0, 1, len(blocks) // 2, len(blocks) - 2, len(blocks) - 1}):
+        q = vi.q_block(wl, 0, block)
+        ref = oracle.attend(Lo, block, q, ko, vo).astype(np.float64)
+        got = gpu_attend(Lg, block, q, kg, vg)
+        err = attn_err(got, ref)
+        assert err <= ATTN_TOL, (block, err)
