@@ -126,7 +126,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* prefi
 }
 
 template <int D, int BITS, int NW>
-__global__ __launch_bounds__(NW * kWave) void attend_kernel(AttendParams p) {
+// Register caps chosen for residency: 2-wave workgroups at 3 waves per SIMD and
+// 4-wave workgroups at 4 (a few dwords spill; measured faster on VAR-d20 than
+// the extra dispatch rounds without the cap).
+__global__ __launch_bounds__(NW * kWave)
+__attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_kernel(AttendParams p) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;              // k-steps of the QK^T contraction
   constexpr int MT = D / 32;              // 32-row tiles of O^T
@@ -437,7 +441,10 @@ constexpr int kSmallWaves = 4;
 constexpr int kSmallStatsHalves = 4096;  // 8 KB per wave
 
 template <int D, int BITS, int QT>
-__global__ __launch_bounds__(kSmallWaves * kWave) void attend_small_kernel(AttendParams p) {
+// 3 waves per SIMD: with 4-wave workgroups every VAR-d20 (sequence, head) is
+// resident in one dispatch round
+__global__ __launch_bounds__(kSmallWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int MT = D / 32;
