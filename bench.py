@@ -4,19 +4,22 @@
 
 One step is one full block-by-block decode pass of the workload: for every
 scale k of the 10-scale VAR schedule and every layer, quantize + bit-pack the
-freshly decoded block's K and V into that layer's packed cache
-(kvq_quantize_block), then run block-causal attention of the block's queries
-over the packed cache (kvq_attend_packed).  Inputs (K, V, Q of every block of
-every layer, bf16, synthetic VAR-shaped data drawn on the device) and caches
-are resident in HBM before the timed region; every layer has its own buffers,
-so the 256 MB last-level cache cannot serve repeats.
+freshly decoded block's K and V into that layer's packed cache, then run
+block-causal attention of the block's queries over the packed cache.  Blocks
+of at most 32 tokens (head_dim 64) do both in one launch (kvq_quantize_attend);
+larger blocks call kvq_quantize_block then kvq_attend_packed (--unfused uses
+the two calls for every block).  Inputs (K, V, Q of every block of every
+layer, bf16, synthetic VAR-shaped data drawn on the device) and caches are
+resident in HBM before the timed region; every layer has its own buffers, so
+the 256 MB last-level cache cannot serve repeats.
 
 Printed: one JSON line.  `value` is packed-KV attention tokens/s over the whole
 step (query tokens x layers per second, quantize+pack included); per-kernel
-figures come from HIP events recorded at every launch boundary on the launch
-stream during the timed steps; `roofline` is for the kernel with the larger share of
-the step; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
-same workload on the host's cores.
+figures (`kernels`, `per_block_us`) come from HIP events recorded at every
+launch boundary on the launch stream during the timed steps; `roofline` is for
+the kernel kind with the largest share of the step, over the launches of that
+kind (`blocks`); `cpu_baseline` is the CPU oracle timed on a bounded sample of
+the same workload on the host's cores.
 """
 from __future__ import annotations
 
@@ -36,9 +39,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "var_d20_b128_int4"
+FUSED_MAX_TOKENS = 32  # blocks kvq_quantize_attend runs as one fused launch (head_dim 64)
 KERNEL_SOURCES = {
     "quant_pack": "visual_autoregressive_kv_amd/csrc/quant_pack.hip",
     "attend": "visual_autoregressive_kv_amd/csrc/attend.hip",
+    "fused": "visual_autoregressive_kv_amd/csrc/attend.hip",
 }
 
 
@@ -51,6 +56,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="quantize and attend with separate calls for every block")
     return ap.parse_args()
 
 
@@ -222,90 +229,109 @@ def main():
 
     kC = [cache(x) for x in kcs]
     vC = [cache(x) for x in vcs]
-    qargs, aargs = [], []
+    # Decode order: for every block, for every layer, that layer's decode step.
+    # Blocks the library fuses (head_dim 64, at most FUSED_MAX_TOKENS tokens) go
+    # through kvq_quantize_attend (one launch); larger blocks through
+    # kvq_quantize_block then kvq_attend_packed (two launches).
+    def fused(j):
+        return (not args.unfused) and wl.head_dim == 64 and wl.blocks[j] <= FUSED_MAX_TOKENS
+
+    calls = []  # (kind, block, function, arguments), in launch order
     for j in range(NB):
         for l in range(wl.layers):
             # shapes are fixed by construction; check them once here through the binding
             assert tuple(Kin[l][j].shape) == (wl.batch, wl.blocks[j], wl.heads, wl.head_dim)
-            qargs.append((Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
-                          kC[l], vC[l], None, sh))
-            aargs.append((Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
-                          Out[l][j].data_ptr(), sh))
-    qfn, afn = lib.kvq_quantize_block, lib.kvq_attend_packed
-    # one checked call through the binding before the raw loop
+            if fused(j):
+                calls.append(("fused", j, lib.kvq_quantize_attend,
+                              (Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
+                               Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
+                               Out[l][j].data_ptr(), None, sh)))
+            else:
+                calls.append(("quant_pack", j, lib.kvq_quantize_block,
+                              (Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
+                               kC[l], vC[l], None, sh)))
+                calls.append(("attend", j, lib.kvq_attend_packed,
+                              (Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
+                               Out[l][j].data_ptr(), sh)))
+    # one checked call of each kind through the binding before the raw loop
     K.kvq_quantize_block(L, 0, Kin[0][0], Vin[0][0], kcs[0], vcs[0])
     K.kvq_attend_packed(L, 0, Qin[0][0], kcs[0], vcs[0], Out[0][0])
+    K.kvq_quantize_attend(L, 0, Kin[0][0], Vin[0][0], Qin[0][0], kcs[0], vcs[0], Out[0][0])
 
-    # One event per launch boundary: ev[2i] before quantize i, ev[2i+1] between
-    # quantize i and attend i, ev[2i+2] after attend i (also before quantize i+1).
+    # One event per launch boundary: ev[c] before call c, ev[c + 1] after it.
+    n_calls = len(calls)
+
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        for i in range(len(qargs)):
-            rc = qfn(*qargs[i])
+        for c, (_, _, fn, cargs) in enumerate(calls):
+            rc = fn(*cargs)
             if events is not None:
-                events[2 * i + 1].record(stream)
-            rc |= afn(*aargs[i])
-            if events is not None:
-                events[2 * i + 2].record(stream)
+                events[c + 1].record(stream)
             if rc:
-                raise RuntimeError(f"kvq launch failed (rc={rc}) at call {i}")
+                raise RuntimeError(f"kvq launch failed (rc={rc}) at call {c}")
 
     for w in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", flush=True)
 
-    n_calls = len(qargs)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls + 1)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    for s_ in range(args.steps):
+        step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    def span(s, i, off):  # off 0: quantize i, off 1: attend i
-        return evs[s][2 * i + off].elapsed_time(evs[s][2 * i + off + 1])
+    # per kind: summed event time, launches, algorithmic bytes and flops
+    byte_model = {"quant_pack": quant_bytes, "attend": attend_bytes,
+                  "fused": lambda w, k: quant_bytes(w, k) + attend_bytes(w, k)}
+    kinds = {}
+    per_block = {}
+    for c, (kind, j, _, _) in enumerate(calls):
+        ms = sum(evs[s_][c].elapsed_time(evs[s_][c + 1]) for s_ in range(args.steps))
+        k = kinds.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
+        k["ms"] += ms
+        k["launches"] += args.steps
+        k["bytes"] += byte_model[kind](wl, j) * args.steps
+        if kind in ("attend", "fused"):
+            k["flops"] += attend_flops(wl, j) * args.steps
+        per_block.setdefault(kind, {}).setdefault(j, []).append(ms / args.steps)
+    per_block_us = {kind: [round(1e3 * sum(v) / len(v), 2) for _, v in sorted(d.items())]
+                    for kind, d in per_block.items()}
+    per_block_blocks = {kind: sorted(d) for kind, d in per_block.items()}
 
-    q_ms = sum(span(s, i, 0) for s in range(args.steps) for i in range(n_calls))
-    a_ms = sum(span(s, i, 1) for s in range(args.steps) for i in range(n_calls))
+    def gbps(k):
+        return k["bytes"] / (k["ms"] * 1e-3) / 1e9 if k["ms"] > 0 else 0.0
 
-    # per-block average kernel times (calls are ordered block-major, layer-minor)
-    def per_block(off):
-        us = []
-        for j in range(NB):
-            tot = sum(span(s, j * wl.layers + l, off)
-                      for s in range(args.steps) for l in range(wl.layers))
-            us.append(round(1e3 * tot / (args.steps * wl.layers), 2))
-        return us
-
-    q_block_us, a_block_us = per_block(0), per_block(1)
-    per_layer = lambda f: sum(f(wl, j) for j in range(NB)) * wl.layers  # noqa: E731
-    qb = per_layer(quant_bytes) * args.steps
-    ab = per_layer(attend_bytes) * args.steps
-    af = per_layer(attend_flops) * args.steps
-    q_gbps = qb / (q_ms * 1e-3) / 1e9
-    a_gbps = ab / (a_ms * 1e-3) / 1e9
-    a_tflops = af / (a_ms * 1e-3) / 1e12
     ms_per_step = wall * 1e3 / args.steps
     tokens = wl.batch * wl.total_tokens * wl.layers  # query tokens x layers per step
     value = tokens * args.steps / wall
 
-    dominant = "attend" if a_ms >= q_ms else "quant_pack"
-    launches = n_calls * args.steps
-    if dominant == "attend":
-        avg_bytes, avg_ms = ab / launches, a_ms / launches
-    else:
-        avg_bytes, avg_ms = qb / launches, q_ms / launches
+    dominant = max(kinds, key=lambda k: kinds[k]["ms"])
+    dk = kinds[dominant]
+    avg_bytes, avg_ms = dk["bytes"] / dk["launches"], dk["ms"] / dk["launches"]
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(dominant, wl.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "kernel": dominant,
+                "blocks": per_block_blocks[dominant],
                 "avg_launch_us": round(avg_ms * 1e3, 3),
                 "algorithmic_bytes_per_launch": round(avg_bytes)}
+    kind_stats = {}
+    for kind, k in sorted(kinds.items()):
+        g = gbps(k)
+        e = {"ms_per_step": round(k["ms"] / args.steps, 4), "GBps": round(g, 1),
+             "pct_hbm_peak": round(100 * g / HBM_PEAK_GBPS, 2),
+             "blocks": per_block_blocks[kind]}
+        if k["flops"]:
+            tf = k["flops"] / (k["ms"] * 1e-3) / 1e12
+            e["TFLOPs"] = round(tf, 2)
+            e["pct_bf16_mfma_peak"] = round(100 * tf / BF16_PEAK_TFLOPS, 2)
+        kind_stats[kind] = e
     out = {
         "metric": "packed-KV attention tokens/s + quantize/pack GB/s, % of HBM peak (1 GPU)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -315,17 +341,9 @@ def main():
                    "heads": wl.heads, "head_dim": wl.head_dim, "bits": wl.bits,
                    "schedule": list(wl.blocks), "tokens_per_seq": wl.total_tokens,
                    "parallelism": "none (1 GPU)"},
-        "quant_pack_GBps": round(q_gbps, 1),
-        "quant_pack_pct_hbm_peak": round(100 * q_gbps / HBM_PEAK_GBPS, 2),
-        "attend_GBps": round(a_gbps, 1),
-        "attend_pct_hbm_peak": round(100 * a_gbps / HBM_PEAK_GBPS, 2),
-        "attend_TFLOPs": round(a_tflops, 2),
-        "attend_pct_bf16_mfma_peak": round(100 * a_tflops / BF16_PEAK_TFLOPS, 2),
-        "attend_tokens_per_s_kernel": round(tokens * args.steps / (a_ms * 1e-3), 1),
-        "quant_ms_per_step": round(q_ms / args.steps, 4),
-        "attend_ms_per_step": round(a_ms / args.steps, 4),
+        "kernels": kind_stats,
         "copy_peak_GBps": round(copy_gbps, 1),
-        "per_block_us": {"quant_pack": q_block_us, "attend": a_block_us},
+        "per_block_us": per_block_us,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -15,6 +15,9 @@
  *   kvq_pack            the bit-packing step alone (codes given one per byte);
  *   kvq_attend_packed   block-causal attention of the block's queries over the
  *                       packed cache of blocks 0..k, dequantizing on the fly;
+ *   kvq_quantize_attend one decode step of one layer: kvq_quantize_block then
+ *                       kvq_attend_packed for the same block, in one launch
+ *                       where a fused kernel covers the shape;
  *   kvq_bytes           the cache's byte accounting (host only).
  *
  * Conventions shared by every call
@@ -161,6 +164,25 @@ int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_ro
 int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
                       kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
                       float* out, hipStream_t stream);
+
+/*
+ * kvq_quantize_attend -- the decode step of one layer for block k (VAR-Q
+ * abstract: the block is quantized when the generation loop hands it over,
+ * then the block's queries attend to the packed cache of blocks 0..k).
+ * Results are those of kvq_quantize_block(layout, block, src_dtype, k_src,
+ * v_src, k_cache, v_cache, status_dev) followed by kvq_attend_packed(layout,
+ * block, q_bf16, k_cache, v_cache, scale, out) on the same stream: the same
+ * cache bytes and statistics, and the same output values.  Where a fused
+ * kernel covers the shape (head_dim 64, blocks of at most 32 tokens) it is
+ * one launch: each (sequence, head) quantizes its own block and attends.
+ * Otherwise the two launches are issued in order.
+ *   Arguments as in the two calls; out must not overlap the caches or inputs.
+ * Errors: the union of both calls' errors, checked before any launch.
+ */
+int kvq_quantize_attend(const kvq_layout* layout, int32_t block, int32_t src_dtype,
+                        const void* k_src, const void* v_src, const uint16_t* q_bf16,
+                        kvq_cache k_cache, kvq_cache v_cache, float scale, float* out,
+                        int32_t* status_dev, hipStream_t stream);
 
 /* ---- test and measurement helpers (not on the decode path) -------------- */
 

@@ -108,3 +108,26 @@ def test_layout_limits():
     L.n_blocks = 65
     assert lib.kvq_bytes(C.byref(L), 1, C.byref(C.c_uint64()), C.byref(C.c_uint64())) == \
         kb.E_INVAL
+
+
+def test_quantize_attend_argument_errors_return_before_launch():
+    lib = K.lib()
+    L = K.make_layout(2, 3, 64, 4, (1, 4, 9))
+    E = kb.E_INVAL
+    f = lib.kvq_quantize_attend
+    ok = (kb.BF16, FAKE, FAKE, FAKE, _cache(), _cache(), 0.0, FAKE, None, None)
+    assert f(C.byref(L), 3, *ok) == E                        # block
+    assert f(C.byref(L), 0, 7, *ok[1:]) == E                 # dtype
+    assert f(C.byref(L), 0, kb.BF16, None, *ok[2:]) == E     # k_src
+    assert f(C.byref(L), 0, kb.BF16, FAKE, FAKE, None, *ok[4:]) == E          # q
+    assert f(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE + 2, *ok[4:]) == E      # q alignment
+    assert f(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(FAKE + 4), _cache(), 0.0, FAKE,
+             None, None) == E
+    assert f(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(), _cache(), float("nan"), FAKE,
+             None, None) == E
+    assert f(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(), _cache(), 0.0, None, None,
+             None) == E
+    assert f(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(), _cache(), 0.0, FAKE, FAKE + 2,
+             None) == E
+    L5 = K.make_layout(2, 3, 64, 5, (1, 4, 9))
+    assert f(C.byref(L5), 0, *ok) == kb.E_UNSUPPORTED

@@ -1,0 +1,133 @@
+"""GPU parity of kvq_quantize_attend (one decode step of one layer): the cache it
+writes is bit-exact against the oracle, its outputs are bit-identical to
+kvq_quantize_block followed by kvq_attend_packed, and within the attention
+tolerance of the binary64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import varq_inputs as vi
+import visual_autoregressive_kv_amd as K
+from gpu_common import (ATTN_TOL, DEV, assert_cache_equal, attn_err, cache_to_host, layouts,
+                        to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_both_ways(oracle, wl, layer=0, scale=0.0):
+    """Block-by-block decode through the fused call and through the two calls."""
+    Lg, Lo = layouts(oracle, wl)
+    kf, vf = K.alloc_cache(Lg), K.alloc_cache(Lg)
+    ks, vs = K.alloc_cache(Lg), K.alloc_cache(Lg)
+    ko, vo = oracle.alloc_cache(Lo), oracle.alloc_cache(Lo)
+    steps = []
+    for j in range(len(wl.blocks)):
+        kb, vb = vi.kv_block(wl, layer, "k", j), vi.kv_block(wl, layer, "v", j)
+        q = vi.q_block(wl, layer, j)
+        assert oracle.quantize_block(Lo, j, kb, vb, ko, vo) == 0
+        of = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        os_ = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        K.kvq_quantize_attend(Lg, j, to_dev(kb), to_dev(vb), to_dev(q), kf, vf, of, scale=scale)
+        K.kvq_quantize_block(Lg, j, to_dev(kb), to_dev(vb), ks, vs)
+        K.kvq_attend_packed(Lg, j, to_dev(q), ks, vs, os_, scale=scale)
+        torch.cuda.synchronize()
+        ref = oracle.attend(Lo, j, q, ko, vo, scale=scale).astype(np.float64)
+        steps.append((j, of.cpu().numpy(), os_.cpu().numpy(), ref))
+    return kf, vf, ks, vs, ko, vo, steps
+
+
+@pytest.mark.parametrize("wl", [
+    vi.WORKLOADS["var256_tiny_int4"],
+    vi.WORKLOADS["var_d20_b128_int4"].with_(batch=2),
+    vi.WORKLOADS["var_d20_b128_int3_rope"].with_(batch=2),
+    vi.WORKLOADS["var_d24_b128_int4"].with_(batch=2, layers=1),
+    vi.Workload("edge", 1, 1, 3, 64, 3, (1, 7, 32, 33, 2), "bf16", rope=True, seed=13),
+    vi.Workload("edge128", 1, 2, 3, 128, 4, (5, 31, 40), "bf16", seed=17),
+], ids=["tiny_f32", "d20_int4", "d20_int3_rope", "d24_int4", "edge_int3", "edge_d128"])
+def test_fused_matches_two_calls_and_oracle(oracle, wl):
+    kf, vf, ks, vs, ko, vo, steps = decode_both_ways(oracle, wl)
+    assert_cache_equal(kf, ko, "fused K")
+    assert_cache_equal(vf, vo, "fused V")
+    assert_cache_equal(ks, ko, "two-call K")
+    for j, of, os_, ref in steps:
+        assert np.isfinite(of).all(), j
+        assert np.array_equal(of.view(np.uint32), os_.view(np.uint32)), j
+        assert attn_err(of, ref) <= ATTN_TOL, j
+
+
+def test_fused_explicit_scale(oracle):
+    wl = vi.Workload("scale", 1, 2, 4, 64, 4, (1, 4, 9, 16, 25), "bf16", seed=23)
+    *_, steps = decode_both_ways(oracle, wl, scale=0.07)
+    for j, of, os_, ref in steps:
+        assert np.array_equal(of.view(np.uint32), os_.view(np.uint32)), j
+        assert attn_err(of, ref) <= ATTN_TOL, j
+
+
+def test_fused_full_batch_early_blocks(oracle):
+    """VAR-d20 at batch 128, the bench's configuration, blocks 1..5 (the fused
+    kernel's range): cache bit-exact against the two-call path and the oracle
+    on sampled sequences, outputs bit-identical."""
+    wl = vi.WORKLOADS["var_d20_b128_int4"]
+    Lg, Lo = layouts(oracle, wl)
+    kf, vf = K.alloc_cache(Lg), K.alloc_cache(Lg)
+    ks, vs = K.alloc_cache(Lg), K.alloc_cache(Lg)
+    for j in range(5):
+        kb, vb = to_dev(vi.kv_block(wl, 0, "k", j)), to_dev(vi.kv_block(wl, 0, "v", j))
+        q = to_dev(vi.q_block(wl, 0, j))
+        of = torch.empty(tuple(q.shape), dtype=torch.float32, device=DEV)
+        os_ = torch.empty_like(of)
+        K.kvq_quantize_attend(Lg, j, kb, vb, q, kf, vf, of)
+        K.kvq_quantize_block(Lg, j, kb, vb, ks, vs)
+        K.kvq_attend_packed(Lg, j, q, ks, vs, os_)
+        torch.cuda.synchronize()
+        assert torch.equal(of.view(torch.int32), os_.view(torch.int32)), j
+    for a, b in ((kf, ks), (vf, vs)):
+        for key in ("codes", "zero", "scale"):
+            assert torch.equal(a[key], b[key]), key
+    # oracle check of the cache of two sequences
+    seqs = [0, 127]
+    wl2 = wl.with_(batch=len(seqs))
+    L2 = oracle.layout_of(wl2)
+    ko, vo = oracle.alloc_cache(L2), oracle.alloc_cache(L2)
+    for j in range(5):
+        oracle.quantize_block(L2, j, vi.kv_block(wl, 0, "k", j, seqs), vi.kv_block(wl, 0, "v", j, seqs),
+                              ko, vo)
+    kh, vh = cache_to_host(kf), cache_to_host(vf)
+    T = wl.offset(5)
+    for got, ref in ((kh, ko), (vh, vo)):
+        assert np.array_equal(got["codes"][seqs][:, :, :T], ref["codes"][:, :, :T])
+        assert np.array_equal(got["zero"][seqs][:, :, :5], ref["zero"][:, :, :5])
+        assert np.array_equal(got["scale"][seqs][:, :, :5], ref["scale"][:, :, :5])
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_fused_status_flags(oracle, src):
+    wl = vi.Workload("status", 1, 2, 3, 64, 4, (16, 16), src, seed=5)
+    Lg, _ = layouts(oracle, wl)
+    k0, v0 = vi.kv_block(wl, 0, "k", 0), vi.kv_block(wl, 0, "v", 0)
+    kb, vb = vi.kv_block(wl, 0, "k", 1), vi.kv_block(wl, 0, "v", 1)
+    q = to_dev(vi.q_block(wl, 0, 1))
+
+    def run(k, v):
+        kg, vg = K.alloc_cache(Lg), K.alloc_cache(Lg)
+        K.kvq_quantize_block(Lg, 0, to_dev(k0), to_dev(v0), kg, vg)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=DEV)
+        K.kvq_quantize_attend(Lg, 1, to_dev(k), to_dev(v), q, kg, vg, out, status=st)
+        torch.cuda.synchronize()
+        return int(st.item())
+
+    assert run(kb, vb) == 0
+
+    def put(arr, val):
+        a = arr.copy()
+        if src == "f32":
+            a[1, 3, 2, 17] = np.float32(val)
+        else:
+            a[1, 3, 2, 17] = vi.f32_to_bf16_bits(np.array([val], np.float32))[0]
+        return a
+
+    for val, flag in [(np.nan, K.S_NONFINITE), (np.inf, K.S_NONFINITE), (70000.0, K.S_RANGE),
+                      (-1e6, K.S_RANGE)]:
+        assert run(put(kb, val), vb) & flag, val
+        assert run(kb, put(vb, val)) & flag, val

@@ -428,6 +428,115 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
 }
 
 // ---------------------------------------------------------------------------
+// Fused launch, quantize side: one wave quantizes and packs one (sequence,
+// head)'s block of at most 32 tokens for K and V, with the same group
+// statistics and code arithmetic as the standalone quantize kernel.
+//   Phase 1: lane c owns channel c: its extremes over the block's tokens (one
+//   coalesced 128-byte row per token) and its statistics, computed once.
+//   Phase 2: lane (token lane tl, chunk cg) packs the codes of channels 8 cg ..
+//   8 cg + 7 of tokens tl, tl + 8, .. with the statistics read from LDS.
+// The statistics and packed rows also go to LDS for the attention that
+// follows in the same launch; the cache writes serve later blocks.
+// ---------------------------------------------------------------------------
+constexpr int kFusedRowBytes = 32;  // LDS bytes per packed row of the fused block (R <= 32)
+
+template <int D, int BITS, bool F32, bool CHECK>
+__device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b, int h, int lane,
+                                                    _Float16* st_lds, uint8_t* rows_lds,
+                                                    float* scratch) {
+  static_assert(D == kWave, "the wave quantizer covers 64-channel heads, one channel per lane");
+  constexpr int CPR = D / 8;
+  constexpr int TL = kWave / CPR;  // token lanes of phase 2
+  constexpr int MAXR = KT / TL;    // rows per lane in phase 2
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  const FuseParams& f = p.fz;
+  const int n = p.n;
+  const int64_t row_stride = (int64_t)p.H * D;
+  const int64_t base = ((int64_t)b * n * p.H + h) * D;
+  int flags = 0;
+#pragma unroll
+  for (int tensor = 0; tensor < 2; ++tensor) {
+    // ---- phase 1: channel `lane` over the block's tokens
+    float mn = __uint_as_float(0x7F800000u), mx = __uint_as_float(0xFF800000u);
+    int bad = 0;
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) {
+      float x;
+      if constexpr (F32)
+        x = static_cast<const float*>(f.src[tensor])[base + t * row_stride + lane];
+      else
+        x = __uint_as_float((uint32_t)static_cast<const uint16_t*>(f.src[tensor])[base + t * row_stride + lane] << 16);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+      if constexpr (CHECK) bad |= !__builtin_isfinite(x);
+    }
+    const GroupStats gst = group_stats<CHECK>(mn, mx, LEVELS, flags);
+    if constexpr (CHECK) {
+      if (bad) flags |= KVQ_S_NONFINITE;
+    }
+    const int64_t so = (((int64_t)b * p.H + h) * p.NB + f.block) * D + lane;
+    f.zero[tensor][so] = gst.zb;
+    f.scale[tensor][so] = gst.sb;
+    _Float16* srow = st_lds + ((f.block * 2 + tensor) * 2) * D;
+    srow[lane] = __builtin_bit_cast(_Float16, gst.zb);
+    srow[D + lane] = __builtin_bit_cast(_Float16, gst.sb);
+    scratch[lane] = gst.zf;
+    scratch[D + lane] = gst.inv;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // ---- phase 2: codes of (token, 8-channel chunk) items
+    const int cg = lane % CPR;
+    const int tl = lane / CPR;
+    float zf[8], inv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      zf[j] = scratch[8 * cg + j];
+      inv[j] = scratch[D + 8 * cg + j];
+    }
+    uint8_t* rows = f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R;
+    uint8_t* lrows = rows_lds + tensor * KT * kFusedRowBytes;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      const int t = tl + TL * i;
+      if (t < n) {
+        const int64_t e = base + t * row_stride + 8 * cg;
+        float x[8];
+        if constexpr (F32) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(f.src[tensor]) + e);
+          const f32x4 a0 = src[0], a1 = src[1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[j] = a0[j];
+            x[j + 4] = a1[j];
+          }
+        } else {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(f.src[tensor]) + e);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(w[j] << 16);
+            x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+          }
+        }
+        const uint32_t acc = pack_codes8<BITS>(x, zf, inv);
+        uint8_t* dst = rows + (int64_t)t * p.R + BITS * cg;
+        uint8_t* ldst = lrows + t * p.R + BITS * cg;
+        if constexpr (BITS == 4) {
+          *reinterpret_cast<uint32_t*>(dst) = acc;  // 4-byte aligned: rows are 32 bytes
+          *reinterpret_cast<uint32_t*>(ldst) = acc;
+        } else {
+          dst[0] = ldst[0] = (uint8_t)acc;
+          dst[1] = ldst[1] = (uint8_t)(acc >> 8);
+          dst[2] = ldst[2] = (uint8_t)(acc >> 16);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // scratch reuse
+  }
+  if constexpr (CHECK) {
+    if (flags) atomicOr(f.status, flags);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Short blocks (up to 32·QT queries, the early scales; launched with QT = 1): one wave owns one
 // (sequence, head) and all its queries, four independent waves share a
 // workgroup, and no workgroup barrier is needed.  Each lane dequantizes its
@@ -438,13 +547,15 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
 // so the transpose needs no barrier.
 // ---------------------------------------------------------------------------
 constexpr int kSmallWaves = 4;
-constexpr int kSmallStatsHalves = 4096;  // 8 KB per wave
+constexpr int kSmallStatsHalves = 2048;  // 4 KB per wave: up to 8 blocks at head_dim 64
 
-template <int D, int BITS, int QT>
+// FUSE: 0 attention only; 1/2 quantize the block first from bf16 (2: with
+// input checks); 3/4 the same from fp32.
+template <int D, int BITS, int QT, int FUSE>
 // 3 waves per SIMD: with 4-wave workgroups every VAR-d20 (sequence, head) is
 // resident in one dispatch round
 __global__ __launch_bounds__(kSmallWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p) {
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(AttendParams p) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int MT = D / 32;
@@ -452,6 +563,8 @@ __attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p)
   __shared__ __align__(16) uint32_t v_t_all[kSmallWaves][D][VROW];
   __shared__ __align__(16) _Float16 st_all[kSmallWaves][kSmallStatsHalves];
   __shared__ int bend_all[kSmallWaves][KVQ_MAX_BLOCKS];
+  // fused launch: the packed rows of block k (K then V) for the attention below
+  __shared__ __align__(16) uint8_t rows_all[kSmallWaves][FUSE != 0 ? 2 * KT * kFusedRowBytes : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -510,8 +623,10 @@ __attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p)
   };
   issue_loads(0);
 
-  // the launcher only picks this kernel when every statistic fits the wave's LDS
-  for (int i = lane; i < nkb * 2 * CPR; i += kWave) {
+  // the launcher only picks this kernel when every statistic fits the wave's
+  // LDS; a fused launch writes block k's own statistics there itself
+  const int nkb_copy = FUSE != 0 ? nkb - 1 : nkb;
+  for (int i = lane; i < nkb_copy * 2 * CPR; i += kWave) {
     const int blk = i / (2 * CPR);
     const int rem = i - blk * 2 * CPR;
     const int tensor = rem / CPR;
@@ -539,6 +654,12 @@ __attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p)
     }
   }
   const bool live1 = QT > 1 && 32 < p.n;
+  // Fused launch: quantize block k now (its loads overlap the ones above).
+  // Rows of block k then come from LDS (keys off .. off + n - 1).
+  const uint8_t* qrows = rows_all[wave];
+  if constexpr (FUSE != 0)
+    quantize_block_wave<D, BITS, FUSE >= 3, FUSE == 2 || FUSE == 4>(
+        p, b, h, lane, st, rows_all[wave], reinterpret_cast<float*>(&v_t[0][0]));
 
   // Every K and V item of a lane is key `col` of the tile, so one block index
   // per lane follows the tiles; it only moves forward.
@@ -585,6 +706,25 @@ __attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p)
     if (j + 1 < n_tiles) issue_loads(j + 1);
     const int tk = t0 + col;  // this lane's key
     const bool live = tk < n_prefix;
+    if constexpr (FUSE != 0) {
+      const int r = tk - (int)p.fz.off;  // row within block k
+      if (r >= 0 && live) {
+        const uint8_t* kr = qrows + r * p.R;
+        const uint8_t* vr = qrows + KT * kFusedRowBytes + r * p.R;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int bo = k_voff[ks] - col * p.R;  // byte offset within the row
+          kc[ks][0] = *reinterpret_cast<const uint32_t*>(kr + bo);
+          if constexpr (BITS != 4) kc[ks][1] = *reinterpret_cast<const uint32_t*>(kr + bo + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+          const int bo = v_voff[i] - col * p.R;
+          vc[i][0] = *reinterpret_cast<const uint32_t*>(vr + bo);
+          if constexpr (BITS != 4) vc[i][1] = *reinterpret_cast<const uint32_t*>(vr + bo + 4);
+        }
+      }
+    }
     while (tk >= blk_next) {
       ++blk;
       blk_next = blk + 1 < nkb ? bend[blk] : INT32_MAX;
@@ -727,13 +867,13 @@ __attribute__((amdgpu_waves_per_eu(3))) void attend_small_kernel(AttendParams p)
   }
 }
 
-template <int D, int BITS, int QT>
+template <int D, int BITS, int QT, int FUSE = 0>
 hipError_t launch_small(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = 1;
   a.stats_in_lds = 1;
   const int64_t grid = ((int64_t)p.B * p.H + kSmallWaves - 1) / kSmallWaves;
-  hipLaunchKernelGGL((attend_small_kernel<D, BITS, QT>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attend_small_kernel<D, BITS, QT, FUSE>), dim3((unsigned)grid),
                      dim3(kSmallWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
@@ -769,6 +909,37 @@ hipError_t launch_t(const AttendParams& p, hipStream_t s) {
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
   if (head_dim == 64) return bits == 4 ? launch_t<64, 4>(p, s) : launch_t<64, 3>(p, s);
   return bits == 4 ? launch_t<128, 4>(p, s) : launch_t<128, 3>(p, s);
+}
+
+namespace {
+template <int BITS>
+hipError_t launch_small_fused(const AttendParams& a, bool f32, bool check, hipStream_t s) {
+  if (f32) return check ? launch_small<64, BITS, 1, 4>(a, s) : launch_small<64, BITS, 1, 3>(a, s);
+  return check ? launch_small<64, BITS, 1, 2>(a, s) : launch_small<64, BITS, 1, 1>(a, s);
+}
+}  // namespace
+
+hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,
+                                  int bits, bool f32src, hipStream_t s) {
+  const bool small = head_dim == 64 && a.n <= KT && a.n_kblocks * 4 * 64 <= kSmallStatsHalves;
+  if (small) {
+    AttendParams p = a;
+    for (int t = 0; t < 2; ++t) {
+      p.fz.src[t] = q.src[t];
+      p.fz.codes[t] = q.codes[t];
+      p.fz.zero[t] = q.zero[t];
+      p.fz.scale[t] = q.scale[t];
+    }
+    p.fz.status = q.status;
+    p.fz.off = q.off;
+    p.fz.block = q.block;
+    const bool check = q.status != nullptr;
+    return bits == 4 ? launch_small_fused<4>(p, f32src, check, s)
+                     : launch_small_fused<3>(p, f32src, check, s);
+  }
+  const hipError_t e = launch_quantize(q, head_dim, bits, f32src, s);
+  if (e != hipSuccess) return e;
+  return launch_attend(a, head_dim, bits, s);
 }
 
 }  // namespace kvq

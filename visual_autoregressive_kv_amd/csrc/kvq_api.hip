@@ -81,6 +81,89 @@ void pick_tiling(int n, int d, int32_t* gs, int32_t* rpt) {
   *rpt = 8;
 }
 
+// argument checks and launch descriptor of kvq_quantize_block
+int make_quant_params(const kvq_layout* layout, int32_t block, int32_t src_dtype,
+                      const void* k_src, const void* v_src, kvq_cache k_cache, kvq_cache v_cache,
+                      int32_t* status_dev, QuantParams* out) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (block < 0 || block >= layout->n_blocks) return KVQ_E_INVAL;
+  if (src_dtype != KVQ_F32 && src_dtype != KVQ_BF16) return KVQ_E_INVAL;
+  if (!k_src || !v_src || !aligned16(k_src) || !aligned16(v_src)) return KVQ_E_INVAL;
+  if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
+  if (status_dev && (reinterpret_cast<uintptr_t>(status_dev) & 3)) return KVQ_E_INVAL;
+  const int sup = gpu_supported(layout);
+  if (sup != KVQ_OK) return sup;
+  QuantParams& p = *out;
+  memset(&p, 0, sizeof(p));
+  p.src[0] = k_src;
+  p.src[1] = v_src;
+  p.codes[0] = k_cache.codes;
+  p.codes[1] = v_cache.codes;
+  p.zero[0] = k_cache.zero;
+  p.zero[1] = v_cache.zero;
+  p.scale[0] = k_cache.scale;
+  p.scale[1] = v_cache.scale;
+  p.status = status_dev;
+  p.BH = layout->batch * layout->heads;
+  p.n_tiles = 2 * (int64_t)p.BH;
+  p.H = layout->heads;
+  p.n = layout->block_tokens[block];
+  p.NB = layout->n_blocks;
+  p.block = block;
+  p.R = row_bytes(layout->bits, layout->head_dim);
+  p.T = offset_of(layout, layout->n_blocks);
+  p.off = offset_of(layout, block);
+  pick_tiling(p.n, layout->head_dim, &p.gs, &p.rpt);
+  return KVQ_OK;
+}
+
+// argument checks and launch descriptor of kvq_attend_packed
+int make_attend_params(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
+                       kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
+                       float* out, AttendParams* dst) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (block < 0 || block >= layout->n_blocks) return KVQ_E_INVAL;
+  if (!q_bf16 || !out || !aligned16(q_bf16) || !aligned16(out)) return KVQ_E_INVAL;
+  if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
+  if (!(scale == scale) || isinf(scale)) return KVQ_E_INVAL;
+  const int sup = gpu_supported(layout);
+  if (sup != KVQ_OK) return sup;
+  AttendParams& p = *dst;
+  memset(&p, 0, sizeof(p));
+  p.q = q_bf16;
+  p.kcodes = k_cache.codes;
+  p.kzero = k_cache.zero;
+  p.kscale = k_cache.scale;
+  p.vcodes = v_cache.codes;
+  p.vzero = v_cache.zero;
+  p.vscale = v_cache.scale;
+  p.out = out;
+  p.T_cache = offset_of(layout, layout->n_blocks);
+  p.B = layout->batch;
+  p.H = layout->heads;
+  p.n = layout->block_tokens[block];
+  p.NB = layout->n_blocks;
+  p.R = row_bytes(layout->bits, layout->head_dim);
+  p.n_prefix = (int32_t)offset_of(layout, block + 1);
+  p.n_kblocks = block + 1;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)layout->head_dim);
+  p.scale_log2 = (float)(sc * 1.4426950408889634);
+  int64_t e = 0;
+  for (int i = 0; i < layout->n_blocks; ++i) {
+    e += layout->block_tokens[i];
+    p.block_end[i] = (int32_t)e;
+  }
+  return KVQ_OK;
+}
+
+kvq_cache_const const_view(kvq_cache c) {
+  kvq_cache_const r;
+  r.codes = c.codes;
+  r.zero = c.zero;
+  r.scale = c.scale;
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,36 +185,10 @@ int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
 int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtype,
                        const void* k_src, const void* v_src, kvq_cache k_cache,
                        kvq_cache v_cache, int32_t* status_dev, hipStream_t stream) {
-  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
-  if (block < 0 || block >= layout->n_blocks) return KVQ_E_INVAL;
-  if (src_dtype != KVQ_F32 && src_dtype != KVQ_BF16) return KVQ_E_INVAL;
-  if (!k_src || !v_src || !aligned16(k_src) || !aligned16(v_src)) return KVQ_E_INVAL;
-  if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
-  if (status_dev && (reinterpret_cast<uintptr_t>(status_dev) & 3)) return KVQ_E_INVAL;
-  const int sup = gpu_supported(layout);
-  if (sup != KVQ_OK) return sup;
-
   QuantParams p;
-  memset(&p, 0, sizeof(p));
-  p.src[0] = k_src;
-  p.src[1] = v_src;
-  p.codes[0] = k_cache.codes;
-  p.codes[1] = v_cache.codes;
-  p.zero[0] = k_cache.zero;
-  p.zero[1] = v_cache.zero;
-  p.scale[0] = k_cache.scale;
-  p.scale[1] = v_cache.scale;
-  p.status = status_dev;
-  p.BH = layout->batch * layout->heads;
-  p.n_tiles = 2 * (int64_t)p.BH;
-  p.H = layout->heads;
-  p.n = layout->block_tokens[block];
-  p.NB = layout->n_blocks;
-  p.block = block;
-  p.R = row_bytes(layout->bits, layout->head_dim);
-  p.T = offset_of(layout, layout->n_blocks);
-  p.off = offset_of(layout, block);
-  pick_tiling(p.n, layout->head_dim, &p.gs, &p.rpt);
+  const int rc = make_quant_params(layout, block, src_dtype, k_src, v_src, k_cache, v_cache,
+                                   status_dev, &p);
+  if (rc != KVQ_OK) return rc;
   return device_status(
       launch_quantize(p, layout->head_dim, layout->bits, src_dtype == KVQ_F32, stream));
 }
@@ -212,39 +269,26 @@ int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const c
 int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
                       kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
                       float* out, hipStream_t stream) {
-  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
-  if (block < 0 || block >= layout->n_blocks) return KVQ_E_INVAL;
-  if (!q_bf16 || !out || !aligned16(q_bf16) || !aligned16(out)) return KVQ_E_INVAL;
-  if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
-  if (!(scale == scale) || isinf(scale)) return KVQ_E_INVAL;
-  const int sup = gpu_supported(layout);
-  if (sup != KVQ_OK) return sup;
   AttendParams p;
-  memset(&p, 0, sizeof(p));
-  p.q = q_bf16;
-  p.kcodes = k_cache.codes;
-  p.kzero = k_cache.zero;
-  p.kscale = k_cache.scale;
-  p.vcodes = v_cache.codes;
-  p.vzero = v_cache.zero;
-  p.vscale = v_cache.scale;
-  p.out = out;
-  p.T_cache = offset_of(layout, layout->n_blocks);
-  p.B = layout->batch;
-  p.H = layout->heads;
-  p.n = layout->block_tokens[block];
-  p.NB = layout->n_blocks;
-  p.R = row_bytes(layout->bits, layout->head_dim);
-  p.n_prefix = (int32_t)offset_of(layout, block + 1);
-  p.n_kblocks = block + 1;
-  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)layout->head_dim);
-  p.scale_log2 = (float)(sc * 1.4426950408889634);
-  int64_t e = 0;
-  for (int i = 0; i < layout->n_blocks; ++i) {
-    e += layout->block_tokens[i];
-    p.block_end[i] = (int32_t)e;
-  }
+  const int rc = make_attend_params(layout, block, q_bf16, k_cache, v_cache, scale, out, &p);
+  if (rc != KVQ_OK) return rc;
   return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+}
+
+int kvq_quantize_attend(const kvq_layout* layout, int32_t block, int32_t src_dtype,
+                        const void* k_src, const void* v_src, const uint16_t* q_bf16,
+                        kvq_cache k_cache, kvq_cache v_cache, float scale, float* out,
+                        int32_t* status_dev, hipStream_t stream) {
+  QuantParams qp;
+  int rc = make_quant_params(layout, block, src_dtype, k_src, v_src, k_cache, v_cache,
+                             status_dev, &qp);
+  if (rc != KVQ_OK) return rc;
+  AttendParams ap;
+  rc = make_attend_params(layout, block, q_bf16, const_view(k_cache), const_view(v_cache), scale,
+                          out, &ap);
+  if (rc != KVQ_OK) return rc;
+  return device_status(launch_quantize_attend(qp, ap, layout->head_dim, layout->bits,
+                                              src_dtype == KVQ_F32, stream));
 }
 
 int kvq_stream_copy(const void* src, void* dst, uint64_t n_bytes, hipStream_t stream) {

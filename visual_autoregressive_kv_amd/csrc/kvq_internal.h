@@ -63,6 +63,70 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // launch descriptors
 // ---------------------------------------------------------------------------
 
+// ---------------------------------------------------------------------------
+// Group statistics and code packing shared by the quantize kernel and the
+// fused quantize-and-attend kernel (one definition, so both write identical
+// bytes).
+// ---------------------------------------------------------------------------
+
+// zero = binary16 rounded down from the group minimum, step = binary16 rounded
+// up from fp32(max - zero) / (2^b - 1), and the fp32 reciprocal of the step
+// (0 for a constant group).  lo, hi: exact extremes with a zero extreme as +0.
+struct GroupStats {
+  uint16_t zb, sb;  // binary16 bit patterns
+  float zf, inv;
+};
+template <bool CHECK>
+__device__ __forceinline__ GroupStats group_stats(float lo, float hi, float levels, int& flags) {
+  GroupStats g;
+  lo = (lo == 0.0f) ? 0.0f : lo;
+  hi = (hi == 0.0f) ? 0.0f : hi;
+  if constexpr (CHECK) {
+    if (!(lo >= -65504.0f) || !(hi <= 65504.0f)) flags |= KVQ_S_RANGE;
+  }
+  g.zb = rd16(lo);
+  g.zf = h2f(g.zb);
+  const float r = hi - g.zf;
+  const float q = r / levels;
+  g.sb = ru16(q);
+  const float sf = h2f(g.sb);
+  if constexpr (CHECK) {
+    if (!(sf <= 65504.0f)) flags |= KVQ_S_RANGE;
+  }
+  g.inv = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+  return g;
+}
+
+template <int BITS>
+struct PackMagic {
+  // sum over the 8 codes of the exponent bits 0x4B000000 of (2^23 + code),
+  // shifted to the code's position, modulo 2^32
+  static constexpr uint32_t value() {
+    uint32_t s = 0;
+    for (int j = 0; j < 8; ++j) s += (0x4B000000u << (BITS * j));
+    return s;
+  }
+};
+
+// codes of 8 channel values, LSB-first in the low 8*BITS bits: clamp(rne((x -
+// z) * inv), 0, 2^b - 1).  Adding 2^23 rounds half-to-even and leaves the
+// integer in the low mantissa bits, which the shift-add collects directly.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_codes8(const float x[8], const float zf[8],
+                                                const float inv[8]) {
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float t = x[j] - zf[j];
+    const float u = t * inv[j];
+    const float c = __builtin_amdgcn_fmed3f(u, 0.0f, LEVELS);
+    const float f = c + 8388608.0f;  // 2^23
+    acc += __float_as_uint(f) << (BITS * j);
+  }
+  return acc - PackMagic<BITS>::value();
+}
+
 struct QuantParams {
   const void* src[2];  // K, V: [B][n][H][D]
   uint8_t* codes[2];   // [B][H][T][R]
@@ -103,6 +167,19 @@ struct DequantParams {
   int32_t block_end[KVQ_MAX_BLOCKS];  // exclusive prefix ends
 };
 
+// Quantize-and-pack side of the fused quantize + attend launch: block `block`
+// of K and V ([B][n][H][D]) goes into cache rows off .. off + n - 1 and stats
+// slot `block` before the block's queries attend.
+struct FuseParams {
+  const void* src[2];  // K, V
+  uint8_t* codes[2];   // writable views of the caches the attention reads
+  uint16_t* zero[2];
+  uint16_t* scale[2];
+  int32_t* status;  // nullable
+  int64_t off;
+  int32_t block;
+};
+
 struct AttendParams {
   const uint16_t* q;  // [B][n][H][D] bf16
   const uint8_t* kcodes;
@@ -120,6 +197,7 @@ struct AttendParams {
   float scale_log2;   // softmax scale * log2(e)
   int32_t stats_in_lds;  // prefix statistics staged in LDS as fp32
   int32_t block_end[KVQ_MAX_BLOCKS];
+  FuseParams fz;  // used by the fused launch only
 };
 
 hipError_t launch_quantize(const QuantParams& p, int head_dim, int bits, bool f32src,
@@ -128,6 +206,10 @@ hipError_t launch_pack(const PackParams& p, hipStream_t s);
 hipError_t launch_unpack(const UnpackParams& p, hipStream_t s);
 hipError_t launch_dequantize(const DequantParams& p, hipStream_t s);
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s);
+// quantize block k (q) then attend its queries (a): one launch where a fused
+// kernel covers the shape, else the two launches in order
+hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,
+                                  int bits, bool f32src, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n, hipStream_t s);
 
 }  // namespace kvq

@@ -29,17 +29,6 @@ constexpr int kWG = 256;
 constexpr int kMaxRpt = 8;
 constexpr int kStageBytes = kWG * kMaxRpt * 4 + 16 * 32;
 
-template <int BITS>
-struct PackMagic {
-  // sum over the 8 codes of the exponent bits 0x4B000000 of (2^23 + code),
-  // shifted to the code's position, modulo 2^32
-  static constexpr uint32_t value() {
-    uint32_t s = 0;
-    for (int j = 0; j < 8; ++j) s += (0x4B000000u << (BITS * j));
-    return s;
-  }
-};
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -209,21 +198,11 @@ __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
       lo = __uint_as_float(__float_as_uint(lo) & 0xFFFF0000u);
       hi = __uint_as_float(__float_as_uint(hi) & 0xFFFF0000u);
     }
-    lo = (lo == 0.0f) ? 0.0f : lo;  // a zero extreme is +0
-    hi = (hi == 0.0f) ? 0.0f : hi;
-    if constexpr (CHECK) {
-      if (!(lo >= -65504.0f) || !(hi <= 65504.0f)) flags |= KVQ_S_RANGE;
-    }
-    zb[j] = rd16(lo);
-    zf[j] = h2f(zb[j]);
-    const float r = hi - zf[j];
-    const float q = r / LEVELS;
-    sb[j] = ru16(q);
-    const float sf = h2f(sb[j]);
-    if constexpr (CHECK) {
-      if (!(sf <= 65504.0f)) flags |= KVQ_S_RANGE;
-    }
-    inv[j] = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+    const GroupStats gs_ = group_stats<CHECK>(lo, hi, LEVELS, flags);
+    zb[j] = gs_.zb;
+    sb[j] = gs_.sb;
+    zf[j] = gs_.zf;
+    inv[j] = gs_.inv;
   }
   if (tile_ok && r0 == 0) {
     const int64_t so = (((int64_t)b * p.H + h) * p.NB + p.block) * D + 8 * cg;
@@ -262,16 +241,10 @@ __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
 #pragma unroll
     for (int i = 0; i < kMaxRpt; ++i) {
       if (i < nvalid) {
-        uint32_t acc = 0;
+        float xv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float t = chan<F32>(v[i], j) - zf[j];
-          const float u = t * inv[j];
-          const float c = __builtin_amdgcn_fmed3f(u, 0.0f, LEVELS);
-          const float f = c + 8388608.0f;  // 2^23: rounds half-to-even into the low bits
-          acc += __float_as_uint(f) << (BITS * j);
-        }
-        acc -= PackMagic<BITS>::value();
+        for (int j = 0; j < 8; ++j) xv[j] = chan<F32>(v[i], j);
+        const uint32_t acc = pack_codes8<BITS>(xv, zf, inv);
         const int chunk = (r0 + i * rps) * CPR + cg;  // within this pass
         uint8_t* sp = my_stage + mis + chunk * BITS;
         if constexpr (BITS == 4) {

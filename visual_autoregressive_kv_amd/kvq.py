@@ -85,6 +85,9 @@ def lib() -> C.CDLL:
         L.kvq_attend_packed.restype = C.c_int
         L.kvq_attend_packed.argtypes = [C.POINTER(Layout), i32, vp, Cache, Cache, C.c_float, vp,
                                         vp]
+        L.kvq_quantize_attend.restype = C.c_int
+        L.kvq_quantize_attend.argtypes = [C.POINTER(Layout), i32, i32, vp, vp, vp, Cache, Cache,
+                                          C.c_float, vp, vp, vp]
         L.kvq_stream_copy.restype = C.c_int
         L.kvq_stream_copy.argtypes = [vp, vp, u64, vp]
         _lib = L
@@ -227,6 +230,27 @@ def kvq_attend_packed(layout: Layout, block: int, q: torch.Tensor, k_cache, v_ca
                                    _cache(layout, k_cache, "k_cache"),
                                    _cache(layout, v_cache, "v_cache"), float(scale),
                                    _dev(out, "out", torch.float32, shp), _stream(stream)))
+
+
+def kvq_quantize_attend(layout: Layout, block: int, k_src: torch.Tensor, v_src: torch.Tensor,
+                        q: torch.Tensor, k_cache, v_cache, out: torch.Tensor, scale: float = 0.0,
+                        status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvq_quantize_block then kvq_attend_packed for one block, one launch where fused."""
+    shp = _block_shape(layout, block)
+    if k_src.dtype != v_src.dtype:
+        raise ValueError("k_src and v_src dtypes differ")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(k_src.dtype)
+    if dt is None:
+        raise ValueError("source dtype must be float32 or bfloat16")
+    kp = _dev(k_src, "k_src", k_src.dtype, shp)
+    vp = _dev(v_src, "v_src", v_src.dtype, shp)
+    sp = None if status is None else _dev(status, "status", torch.int32, (1,))
+    _check("kvq_quantize_attend",
+           lib().kvq_quantize_attend(C.byref(layout), block, dt, kp, vp,
+                                     _dev(q, "q", torch.bfloat16, shp),
+                                     _cache(layout, k_cache, "k_cache"),
+                                     _cache(layout, v_cache, "v_cache"), float(scale),
+                                     _dev(out, "out", torch.float32, shp), sp, _stream(stream)))
 
 
 def kvq_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
