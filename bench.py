@@ -5,10 +5,9 @@
 One step is one full block-by-block decode pass of the workload: for every
 scale k of the 10-scale VAR schedule and every layer, quantize + bit-pack the
 freshly decoded block's K and V into that layer's packed cache, then run
-block-causal attention of the block's queries over the packed cache.  Blocks
-of at most 32 tokens (head_dim 64) do both in one launch (kvq_quantize_attend);
-larger blocks call kvq_quantize_block then kvq_attend_packed (--unfused uses
-the two calls for every block).  Inputs (K, V, Q of every block of every
+block-causal attention of the block's queries over the packed cache, both in
+one launch (kvq_quantize_attend; head_dim 64, blocks of up to 256 tokens);
+--unfused calls kvq_quantize_block then kvq_attend_packed for every block.  Inputs (K, V, Q of every block of every
 layer, bf16, synthetic VAR-shaped data drawn on the device) and caches are
 resident in HBM before the timed region; every layer has its own buffers, so
 the 256 MB last-level cache cannot serve repeats.
@@ -39,7 +38,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "var_d20_b128_int4"
-FUSED_MAX_TOKENS = 32  # blocks kvq_quantize_attend runs as one fused launch (head_dim 64)
+FUSED_MAX_TOKENS = 256  # blocks kvq_quantize_attend runs as one launch (head_dim 64, bf16)
 KERNEL_SOURCES = {
     "quant_pack": "visual_autoregressive_kv_amd/csrc/quant_pack.hip",
     "attend": "visual_autoregressive_kv_amd/csrc/attend.hip",
@@ -234,7 +233,8 @@ def main():
     # through kvq_quantize_attend (one launch); larger blocks through
     # kvq_quantize_block then kvq_attend_packed (two launches).
     def fused(j):
-        return (not args.unfused) and wl.head_dim == 64 and wl.blocks[j] <= FUSED_MAX_TOKENS
+        return (not args.unfused and wl.head_dim == 64 and wl.blocks[j] <= FUSED_MAX_TOKENS
+                and (wl.src == "bf16" or wl.blocks[j] <= 32))
 
     calls = []  # (kind, block, function, arguments), in launch order
     for j in range(NB):

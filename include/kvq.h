@@ -173,8 +173,9 @@ int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q
  * v_src, k_cache, v_cache, status_dev) followed by kvq_attend_packed(layout,
  * block, q_bf16, k_cache, v_cache, scale, out) on the same stream: the same
  * cache bytes and statistics, and the same output values.  Where a fused
- * kernel covers the shape (head_dim 64, blocks of at most 32 tokens) it is
- * one launch: each (sequence, head) quantizes its own block and attends.
+ * kernel covers the shape it is one launch in which each (sequence, head)
+ * quantizes its own block and then attends: head_dim 64 with blocks of at
+ * most 32 tokens (bf16 or fp32 input) or of 33..256 tokens (bf16 input).
  * Otherwise the two launches are issued in order.
  *   Arguments as in the two calls; out must not overlap the caches or inputs.
  * Errors: the union of both calls' errors, checked before any launch.

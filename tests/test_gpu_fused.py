@@ -100,9 +100,11 @@ def test_fused_full_batch_early_blocks(oracle):
         assert np.array_equal(got["scale"][seqs][:, :, :5], ref["scale"][:, :, :5])
 
 
-@pytest.mark.parametrize("src", ["bf16", "f32"])
-def test_fused_status_flags(oracle, src):
-    wl = vi.Workload("status", 1, 2, 3, 64, 4, (16, 16), src, seed=5)
+@pytest.mark.parametrize("src,second", [("bf16", 16), ("f32", 16), ("bf16", 64), ("bf16", 200)])
+def test_fused_status_flags(oracle, src, second):
+    """Input screening through the fused call: the one-wave path (16 tokens) and
+    the workgroup path (64 and 200 tokens)."""
+    wl = vi.Workload("status", 1, 2, 3, 64, 4, (16, second), src, seed=5)
     Lg, _ = layouts(oracle, wl)
     k0, v0 = vi.kv_block(wl, 0, "k", 0), vi.kv_block(wl, 0, "v", 0)
     kb, vb = vi.kv_block(wl, 0, "k", 1), vi.kv_block(wl, 0, "v", 1)

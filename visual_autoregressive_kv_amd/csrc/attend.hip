@@ -125,7 +125,145 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* prefi
                                            prefix_bytes - off, 0x00020000 /* 32-bit data format */);
 }
 
-template <int D, int BITS, int NW>
+// ---------------------------------------------------------------------------
+// Fused launch, quantize side for a workgroup that owns one (sequence, head):
+// the first half of the threads quantizes block k of K, the second half of V
+// (bf16 input, the same group statistics and code arithmetic as the standalone
+// quantize kernel).  Thread (row group rg, chunk c) of a half holds channels
+// 8 c .. 8 c + 7 of rows rg, rg + RG, .. (at most 8) in registers; extremes
+// meet through an xor butterfly inside the wave and LDS across waves; one wave
+// per half then computes each channel's statistics once (lane = channel), and
+// every thread packs its rows.  The packed rows reach the cache before the
+// caller's barrier, so the attention reads them back like older blocks.
+// scratch: (NW + 2) * 2 * 64 floats of LDS.
+// ---------------------------------------------------------------------------
+template <int D, int BITS, int NW, bool CHECK>
+__device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, int h, int tid,
+                                                  _Float16* st_lds, float* scratch) {
+  static_assert(D == kWave && NW >= 2, "64-channel heads, at least one wave per tensor");
+  constexpr int CPR = D / 8;
+  constexpr int GT = NW * kWave / 2;  // threads per tensor
+  constexpr int RG = GT / CPR;        // row groups
+  constexpr int MAXR = 8;             // rows per thread (n <= RG * MAXR)
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  const FuseParams& f = p.fz;
+  const int n = p.n;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int tensor = tid / GT;
+  const int u = tid % GT;
+  const int c = u % CPR;
+  const int rg = u / CPR;
+  const int64_t row_stride = (int64_t)p.H * D;
+  const int64_t base = ((int64_t)b * n * p.H + h) * D + 8 * c;
+  const uint16_t* src = static_cast<const uint16_t*>(f.src[tensor]);
+
+  u32x4 w[MAXR];
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int r = rg + RG * i;
+    if (r < n) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + base + r * row_stride));
+  }
+  auto chan = [&](const u32x4& v, int j) {
+    const uint32_t x = v[j >> 1];
+    return __uint_as_float((j & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  };
+  float mn[8], mx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mn[j] = __uint_as_float(0x7F800000u);
+    mx[j] = __uint_as_float(0xFF800000u);
+  }
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    if (rg + RG * i < n) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = chan(w[i], j);
+        mn[j] = fminf(mn[j], x);
+        mx[j] = fmaxf(mx[j], x);
+        if constexpr (CHECK) bad |= !__builtin_isfinite(x);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = CPR; m < kWave; m <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
+      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
+    }
+  }
+  float* red = scratch;                    // [NW][2][64]: per-wave extremes
+  float* zi = scratch + NW * 2 * kWave;    // [2][2][64]: zero and reciprocal step
+  if (lane < CPR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      red[(wave * 2 + 0) * kWave + 8 * lane + j] = mn[j];
+      red[(wave * 2 + 1) * kWave + 8 * lane + j] = mx[j];
+    }
+  }
+  __syncthreads();
+  int flags = 0;
+  if (u < kWave) {  // first wave of each half: lane = channel
+    const int ch = lane;
+    float lo = __uint_as_float(0x7F800000u), hi = __uint_as_float(0xFF800000u);
+#pragma unroll
+    for (int wv = 0; wv < NW / 2; ++wv) {
+      const int ww = tensor * (NW / 2) + wv;
+      lo = fminf(lo, red[(ww * 2 + 0) * kWave + ch]);
+      hi = fmaxf(hi, red[(ww * 2 + 1) * kWave + ch]);
+    }
+    const GroupStats gst = group_stats<CHECK>(lo, hi, LEVELS, flags);
+    const int64_t so = (((int64_t)b * p.H + h) * p.NB + f.block) * D + ch;
+    f.zero[tensor][so] = gst.zb;
+    f.scale[tensor][so] = gst.sb;
+    if (st_lds) {
+      _Float16* srow = st_lds + ((f.block * 2 + tensor) * 2) * D;
+      srow[ch] = __builtin_bit_cast(_Float16, gst.zb);
+      srow[D + ch] = __builtin_bit_cast(_Float16, gst.sb);
+    }
+    zi[(tensor * 2 + 0) * kWave + ch] = gst.zf;
+    zi[(tensor * 2 + 1) * kWave + ch] = gst.inv;
+  }
+  __syncthreads();
+  float zf[8], inv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    zf[j] = zi[(tensor * 2 + 0) * kWave + 8 * c + j];
+    inv[j] = zi[(tensor * 2 + 1) * kWave + 8 * c + j];
+  }
+  uint8_t* rows = f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R + BITS * c;
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int r = rg + RG * i;
+    if (r < n) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = chan(w[i], j);
+      const uint32_t acc = pack_codes8<BITS>(x, zf, inv);
+      uint8_t* dst = rows + (int64_t)r * p.R;
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = acc;  // 4-byte aligned: rows are 32 bytes
+      } else {
+        dst[0] = (uint8_t)acc;
+        dst[1] = (uint8_t)(acc >> 8);
+        dst[2] = (uint8_t)(acc >> 16);
+      }
+    }
+  }
+  if constexpr (CHECK) {
+    if (bad) flags |= KVQ_S_NONFINITE;
+    if (flags) atomicOr(f.status, flags);
+  }
+  // the workgroup reads these rows back after the caller's barrier
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
+
+// FUSE: 0 attention only; 1/2 quantize block k from bf16 first (2: with input
+// checks); the launcher uses it with one query tile per (sequence, head).
+template <int D, int BITS, int NW, int FUSE>
 // Register caps chosen for residency: 2-wave workgroups at 3 waves per SIMD and
 // 4-wave workgroups at 4 (a few dwords spill; measured faster on VAR-d20 than
 // the extra dispatch rounds without the cap).
@@ -162,6 +300,14 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const int n_prefix = p.n_prefix;
   const int n_tiles = (n_prefix + KT - 1) / KT;
 
+  // Fused launch: quantize block k first (k_hi is free until tile 0 is
+  // dequantized; the statistics slot of block k in LDS is filled here, the
+  // copy below skips it; the barrier after the copy publishes everything).
+  if constexpr (FUSE != 0) {
+    quantize_block_wg<D, BITS, NW, FUSE == 2>(p, b, h, tid, stats_lds ? st : nullptr,
+                                              reinterpret_cast<float*>(&k_hi[0][0][0]));
+  }
+
   // ---- item slots: (tensor, key, chunk), fixed for every tile ----------------
   // K items: key = rem / CPR (a row chunk); V items: key = rem % KT, so
   // neighbouring lanes hold neighbouring keys and can pair them.
@@ -183,6 +329,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   }
 
   uint32_t pre[MAXI], pre2[MAXI];  // prefetched packed bits of the next tile
+  // fused launch: block k's rows are written below; tile 0 is fetched after
+  // that unless it ends before block k
+  const bool early0 = FUSE == 0 || (int)p.fz.off >= KT;
   auto issue_loads = [&](int j) {
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpfx, pfx_bytes, tile_bytes, j);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpfx, pfx_bytes, tile_bytes, j);
@@ -194,12 +343,13 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         pre2[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i] + 4, 0, 0);
     }
   };
-  issue_loads(0);
+  if (early0) issue_loads(0);
 
   // ---- block ends and statistics to LDS, Q operand to registers -------------
   for (int i = tid; i < nkb; i += NT) blk_end[i] = p.block_end[i];
-  if (stats_lds) {  // 8 binary16 values per copy
-    for (int i = tid; i < nkb * 2 * CPR; i += NT) {
+  if (stats_lds) {  // 8 binary16 values per copy; a fused launch writes block k's
+    const int nkb_copy = FUSE != 0 ? nkb - 1 : nkb;
+    for (int i = tid; i < nkb_copy * 2 * CPR; i += NT) {
       const int blk = i / (2 * CPR);
       const int rem = i - blk * 2 * CPR;
       const int tensor = rem / CPR;
@@ -222,7 +372,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       qop[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __syncthreads();  // blk_end and statistics visible
+  __syncthreads();  // blk_end, statistics and (fused) block k's rows visible
+  if (!early0) issue_loads(0);
 
   // binary16 statistics (8 channels of z and s) of one block for one tensor
   auto load_stats = [&](int blk, int tensor, int cg, f16x8& z, f16x8& s) {
@@ -878,7 +1029,7 @@ hipError_t launch_small(const AttendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int BITS, int NW>
+template <int D, int BITS, int NW, int FUSE = 0>
 hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = (p.n + NW * 32 - 1) / (NW * 32);
@@ -886,8 +1037,8 @@ hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   a.stats_in_lds = stats_halves <= kStatsLdsHalves;
   const size_t dyn = a.stats_in_lds ? (size_t)stats_halves * sizeof(_Float16) : 0;
   const int64_t grid = (int64_t)p.B * p.H * a.q_tiles;
-  hipLaunchKernelGGL((attend_kernel<D, BITS, NW>), dim3((unsigned)grid), dim3(NW * kWave), dyn,
-                     s, a);
+  hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE>), dim3((unsigned)grid), dim3(NW * kWave),
+                     dyn, s, a);
   return hipGetLastError();
 }
 
@@ -919,23 +1070,43 @@ hipError_t launch_small_fused(const AttendParams& a, bool f32, bool check, hipSt
 }
 }  // namespace
 
+static void fill_fuse(AttendParams& p, const QuantParams& q) {
+  for (int t = 0; t < 2; ++t) {
+    p.fz.src[t] = q.src[t];
+    p.fz.codes[t] = q.codes[t];
+    p.fz.zero[t] = q.zero[t];
+    p.fz.scale[t] = q.scale[t];
+  }
+  p.fz.status = q.status;
+  p.fz.off = q.off;
+  p.fz.block = q.block;
+}
+
+template <int BITS>
+static hipError_t launch_wg_fused(const AttendParams& p, int waves, bool check, hipStream_t s) {
+  if (waves <= 2) return check ? launch_nw<64, BITS, 2, 2>(p, s) : launch_nw<64, BITS, 2, 1>(p, s);
+  if (waves <= 4) return check ? launch_nw<64, BITS, 4, 2>(p, s) : launch_nw<64, BITS, 4, 1>(p, s);
+  return check ? launch_nw<64, BITS, 8, 2>(p, s) : launch_nw<64, BITS, 8, 1>(p, s);
+}
+
 hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,
                                   int bits, bool f32src, hipStream_t s) {
   const bool small = head_dim == 64 && a.n <= KT && a.n_kblocks * 4 * 64 <= kSmallStatsHalves;
   if (small) {
     AttendParams p = a;
-    for (int t = 0; t < 2; ++t) {
-      p.fz.src[t] = q.src[t];
-      p.fz.codes[t] = q.codes[t];
-      p.fz.zero[t] = q.zero[t];
-      p.fz.scale[t] = q.scale[t];
-    }
-    p.fz.status = q.status;
-    p.fz.off = q.off;
-    p.fz.block = q.block;
+    fill_fuse(p, q);
     const bool check = q.status != nullptr;
     return bits == 4 ? launch_small_fused<4>(p, f32src, check, s)
                      : launch_small_fused<3>(p, f32src, check, s);
+  }
+  // larger blocks: the workgroup kernels with one query tile per (sequence, head)
+  const int waves = (a.n + 31) / 32;
+  if (head_dim == 64 && !f32src && a.n <= kMaxWaves * 32 && waves >= 2) {
+    AttendParams p = a;
+    fill_fuse(p, q);
+    const bool check = q.status != nullptr;
+    if (bits == 4) return launch_wg_fused<4>(p, waves, check, s);
+    return launch_wg_fused<3>(p, waves, check, s);
   }
   const hipError_t e = launch_quantize(q, head_dim, bits, f32src, s);
   if (e != hipSuccess) return e;
