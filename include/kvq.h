@@ -80,7 +80,14 @@ extern "C" {
  *   head_dim    D (multiple of 8; the GPU kernels are built for 64 and 128)
  *   bits        code width: 3 or 4 on the GPU (the byte accounting takes 1..8)
  *   n_blocks    NB, number of decode blocks (1..KVQ_MAX_BLOCKS)
- *   pack_mode   0 = dense rows (the only mode built)
+ *   pack_mode   0 = dense rows: each (b, h, token) row of D codes LSB-first in
+ *               ceil(bits*D/8) bytes (the decode path's layout);
+ *               1 = word-aligned: each (b, h) cache is one stream of T*D codes
+ *               in 32-bit words of floor(32/bits) codes, low bits first (3-bit
+ *               codes: 10 per word, 3.2 stored bits, the storage the VAR-Q
+ *               results table's INT3 rows correspond to).  Mode 1 is taken by
+ *               kvq_bytes, kvq_pack and kvq_unpack; the decode calls return
+ *               KVQ_E_UNSUPPORTED for it.
  *   block_tokens[k]  tokens of block k (>= 1), e.g. s*s for next-scale
  *                    prediction at scale s, or a frame's tokens for video
  */
@@ -105,11 +112,12 @@ typedef struct {
 /*
  * kvq_bytes -- bytes held by one (layer, K or V) cache once blocks
  * 0..n_filled-1 are stored: code_bytes = B*H*T*R with T = sum of their
- * block_tokens, stat_bytes = B*H*n_filled*D*4 (one binary16 zero + one binary16
- * step per (block, channel) group).  With n_filled = n_blocks these are the
- * allocation sizes of codes and of zero+scale together.  Host only, pure.
- * Follows the KV-memory accounting of the VAR-Q results table (VAR-d20 at 2x128
- * sequences: 16.60 -> 4.64 GiB at INT4, 72.06% saving).
+ * block_tokens (pack_mode 1: B*H*4*ceil(T*D/floor(32/bits))), stat_bytes =
+ * B*H*n_filled*D*4 (one binary16 zero + one binary16 step per (block, channel)
+ * group).  With n_filled = n_blocks these are the allocation sizes of codes and
+ * of zero+scale together.  Host only, pure.  Follows the KV-memory accounting
+ * of the VAR-Q results table (VAR-d20 at 2x128 sequences: 16.60 -> 4.64 GiB at
+ * INT4, 72.06% saving; INT3 in pack_mode 1: 3.81 GiB, 77.06%).
  * Returns KVQ_OK or KVQ_E_INVAL (bad layout, n_filled out of [0, NB], NULL out).
  */
 int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
@@ -139,7 +147,10 @@ int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtyp
  * rows of ceil(bits*row_len/8) bytes at dst + r*dst_row_stride, bytes between
  * rows untouched.  Same bit layout as the cache rows written by
  * kvq_quantize_block ("bit-packing kernels", VAR-Q abstract).
- *   bits 1..8, pack_mode 0, n_rows >= 0, row_len >= 1,
+ *   pack_mode 1: the n_rows*row_len codes, row after row, form one stream
+ *   written as ceil(n/floor(32/bits)) 32-bit words at dst; dst_row_stride
+ *   must be 0.
+ *   bits 1..8, pack_mode 0 or 1, n_rows >= 0, row_len >= 1,
  *   dst_row_stride >= ceil(bits*row_len/8).
  * codes/dst: device pointers (16-byte aligned).
  */

@@ -54,6 +54,10 @@ def lib():
             f.argtypes = [C.c_void_p, C.c_int64, C.c_void_p]
         L.kvqr_row_bytes.restype = C.c_int32
         L.kvqr_row_bytes.argtypes = [C.c_int32, C.c_int32]
+        L.kvqr_codes_per_word.restype = C.c_int32
+        L.kvqr_codes_per_word.argtypes = [C.c_int32]
+        L.kvqr_stream_words.restype = C.c_int64
+        L.kvqr_stream_words.argtypes = [C.c_int32, C.c_int64]
         L.kvqr_quantize_group.restype = C.c_int
         L.kvqr_quantize_group.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
                                           C.c_void_p, C.c_void_p, C.c_void_p]
@@ -159,25 +163,43 @@ def quantize_block(L: Layout, block: int, k_src: np.ndarray, v_src: np.ndarray,
 
 
 def pack(bits: int, codes: np.ndarray, dst_row_stride: int = 0, pack_mode: int = 0):
+    """pack_mode 0: rows [n_rows, stride]; pack_mode 1: one word-aligned stream (bytes)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     n_rows, row_len = codes.shape
-    R = row_bytes(bits, row_len)
-    stride = dst_row_stride or R
-    dst = np.zeros((n_rows, stride), np.uint8)
-    st = lib().kvqr_pack(bits, pack_mode, _p(codes), n_rows, row_len, _p(dst), stride)
+    if pack_mode == 1:
+        dst = np.zeros(4 * stream_words(bits, n_rows * row_len), np.uint8)
+        st = lib().kvqr_pack(bits, 1, _p(codes), n_rows, row_len, _p(dst), 0)
+    else:
+        R = row_bytes(bits, row_len)
+        stride = dst_row_stride or R
+        dst = np.zeros((n_rows, stride), np.uint8)
+        st = lib().kvqr_pack(bits, pack_mode, _p(codes), n_rows, row_len, _p(dst), stride)
     if st != OK:
         raise ValueError(f"kvqr_pack: {st}")
     return dst
 
 
-def unpack(bits: int, packed: np.ndarray, row_len: int, pack_mode: int = 0):
+def unpack(bits: int, packed: np.ndarray, row_len: int, pack_mode: int = 0, n_rows: int = None):
+    """pack_mode 0: packed [n_rows, stride]; pack_mode 1: a stream of n_rows * row_len codes."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    n_rows, stride = packed.shape
-    codes = np.zeros((n_rows, row_len), np.uint8)
-    st = lib().kvqr_unpack(bits, pack_mode, _p(packed), stride, n_rows, row_len, _p(codes))
+    if pack_mode == 1:
+        codes = np.zeros((n_rows, row_len), np.uint8)
+        st = lib().kvqr_unpack(bits, 1, _p(packed), 0, n_rows, row_len, _p(codes))
+    else:
+        n_rows, stride = packed.shape
+        codes = np.zeros((n_rows, row_len), np.uint8)
+        st = lib().kvqr_unpack(bits, pack_mode, _p(packed), stride, n_rows, row_len, _p(codes))
     if st != OK:
         raise ValueError(f"kvqr_unpack: {st}")
     return codes
+
+
+def codes_per_word(bits: int) -> int:
+    return int(lib().kvqr_codes_per_word(bits))
+
+
+def stream_words(bits: int, n_codes: int) -> int:
+    return int(lib().kvqr_stream_words(bits, n_codes))
 
 
 def dequantize(L: Layout, n_filled: int, cache) -> np.ndarray:

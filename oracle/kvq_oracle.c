@@ -136,13 +136,23 @@ static float bf16_to_f32(uint16_t b) {
 
 int32_t kvqr_row_bytes(int32_t bits, int32_t head_dim) { return (bits * head_dim + 7) / 8; }
 
+/* Word-aligned layout (pack_mode 1): the codes of a whole stream go into 32-bit
+ * words holding floor(32 / bits) codes each, low bits first; the word's top
+ * 32 mod bits bits stay zero (3-bit codes: 10 per word, 2 spare bits, i.e. 3.2
+ * stored bits per code as in the VAR-Q results table's INT3 rows). */
+int32_t kvqr_codes_per_word(int32_t bits) { return 32 / bits; }
+int64_t kvqr_stream_words(int32_t bits, int64_t n_codes) {
+  const int64_t cpw = kvqr_codes_per_word(bits);
+  return (n_codes + cpw - 1) / cpw;
+}
+
 int kvqr_validate(const kvqr_layout* L) {
   if (!L) return KVQR_E_INVAL;
   if (L->batch < 1 || L->heads < 1) return KVQR_E_INVAL;
   if (L->head_dim < 8 || L->head_dim % 8 != 0) return KVQR_E_INVAL;
   if (L->bits < 1 || L->bits > 8) return KVQR_E_INVAL;
   if (L->n_blocks < 1 || L->n_blocks > KVQR_MAX_BLOCKS) return KVQR_E_INVAL;
-  if (L->pack_mode != 0) return KVQR_E_INVAL;
+  if (L->pack_mode != 0 && L->pack_mode != 1) return KVQR_E_INVAL;
   for (int i = 0; i < L->n_blocks; i++)
     if (L->block_tokens[i] < 1) return KVQR_E_INVAL;
   return KVQR_OK;
@@ -241,9 +251,38 @@ void kvqr_unpack_row(int32_t bits, const uint8_t* in, int32_t n, uint8_t* codes)
   }
 }
 
+/* pack_mode 1: the n_rows x row_len codes, row after row, are one stream */
+static void pack_words(int32_t bits, const uint8_t* codes, int64_t n, uint8_t* dst) {
+  const int64_t cpw = kvqr_codes_per_word(bits);
+  const int64_t words = kvqr_stream_words(bits, n);
+  for (int64_t w = 0; w < words; w++) {
+    uint32_t word = 0;
+    for (int64_t k = 0; k < cpw; k++) {
+      const int64_t i = w * cpw + k;
+      if (i < n) word |= (uint32_t)(codes[i] & ((1u << bits) - 1u)) << (bits * k);
+    }
+    for (int byte = 0; byte < 4; byte++) dst[4 * w + byte] = (uint8_t)(word >> (8 * byte));
+  }
+}
+static void unpack_words(int32_t bits, const uint8_t* src, int64_t n, uint8_t* codes) {
+  const int64_t cpw = kvqr_codes_per_word(bits);
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t w = i / cpw, k = i % cpw;
+    uint32_t word = 0;
+    for (int byte = 0; byte < 4; byte++) word |= (uint32_t)src[4 * w + byte] << (8 * byte);
+    codes[i] = (uint8_t)((word >> (bits * k)) & ((1u << bits) - 1u));
+  }
+}
+
 int kvqr_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,
               int32_t row_len, uint8_t* dst, int64_t dst_row_stride) {
-  if (bits < 1 || bits > 8 || pack_mode != 0 || n_rows < 0 || row_len < 1) return KVQR_E_INVAL;
+  if (bits < 1 || bits > 8 || n_rows < 0 || row_len < 1) return KVQR_E_INVAL;
+  if (pack_mode == 1) {  /* one stream; no row stride */
+    if (dst_row_stride != 0) return KVQR_E_INVAL;
+    pack_words(bits, codes, n_rows * row_len, dst);
+    return KVQR_OK;
+  }
+  if (pack_mode != 0) return KVQR_E_INVAL;
   if (dst_row_stride < kvqr_row_bytes(bits, row_len)) return KVQR_E_INVAL;
   for (int64_t r = 0; r < n_rows; r++)
     kvqr_pack_row(bits, codes + r * row_len, row_len, dst + r * dst_row_stride);
@@ -252,7 +291,13 @@ int kvqr_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_r
 
 int kvqr_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_row_stride,
                 int64_t n_rows, int32_t row_len, uint8_t* codes) {
-  if (bits < 1 || bits > 8 || pack_mode != 0 || n_rows < 0 || row_len < 1) return KVQR_E_INVAL;
+  if (bits < 1 || bits > 8 || n_rows < 0 || row_len < 1) return KVQR_E_INVAL;
+  if (pack_mode == 1) {
+    if (src_row_stride != 0) return KVQR_E_INVAL;
+    unpack_words(bits, src, n_rows * row_len, codes);
+    return KVQR_OK;
+  }
+  if (pack_mode != 0) return KVQR_E_INVAL;
   if (src_row_stride < kvqr_row_bytes(bits, row_len)) return KVQR_E_INVAL;
   for (int64_t r = 0; r < n_rows; r++)
     kvqr_unpack_row(bits, src + r * src_row_stride, row_len, codes + r * row_len);
@@ -311,6 +356,7 @@ int kvqr_quantize_block(const kvqr_layout* L, int32_t block, int32_t src_dtype,
                         const void* k_src, const void* v_src, kvqr_cache k_cache,
                         kvqr_cache v_cache) {
   if (kvqr_validate(L) != KVQR_OK) return KVQR_E_INVAL;
+  if (L->pack_mode != 0) return KVQR_E_INVAL; /* the decode path keeps dense rows */
   if (block < 0 || block >= L->n_blocks) return KVQR_E_INVAL;
   if (src_dtype != KVQR_F32 && src_dtype != KVQR_BF16) return KVQR_E_INVAL;
   if (!k_src || !v_src || !k_cache.codes || !k_cache.zero || !k_cache.scale || !v_cache.codes ||
@@ -358,7 +404,7 @@ static void dequant_bh(const kvqr_layout* L, kvqr_cache c, int32_t b, int32_t h,
 }
 
 int kvqr_dequantize(const kvqr_layout* L, int32_t n_filled, kvqr_cache c, float* out) {
-  if (kvqr_validate(L) != KVQR_OK) return KVQR_E_INVAL;
+  if (kvqr_validate(L) != KVQR_OK || L->pack_mode != 0) return KVQR_E_INVAL;
   if (n_filled < 0 || n_filled > L->n_blocks || !out) return KVQR_E_INVAL;
   const int32_t B = L->batch, H = L->heads, D = L->head_dim;
   const int64_t T = kvqr_total_tokens(L, n_filled);
@@ -393,7 +439,7 @@ static void attend_one(int32_t D, int64_t T, const double* q, const float* kh, c
 
 static int attend_args_ok(const kvqr_layout* L, int32_t block, const uint16_t* q, kvqr_cache k,
                           kvqr_cache v) {
-  if (kvqr_validate(L) != KVQR_OK) return 0;
+  if (kvqr_validate(L) != KVQR_OK || L->pack_mode != 0) return 0;
   if (block < 0 || block >= L->n_blocks || !q) return 0;
   if (!k.codes || !k.zero || !k.scale || !v.codes || !v.zero || !v.scale) return 0;
   return 1;
@@ -467,7 +513,10 @@ int kvqr_bytes(const kvqr_layout* L, int32_t n_filled, uint64_t* code_bytes,
   if (n_filled < 0 || n_filled > L->n_blocks || !code_bytes || !stat_bytes) return KVQR_E_INVAL;
   uint64_t BH = (uint64_t)L->batch * (uint64_t)L->heads;
   uint64_t T = (uint64_t)kvqr_total_tokens(L, n_filled);
-  *code_bytes = BH * T * (uint64_t)kvqr_row_bytes(L->bits, L->head_dim);
+  if (L->pack_mode == 1) /* each (b, h) cache is one word-aligned stream of T*D codes */
+    *code_bytes = BH * 4u * (uint64_t)kvqr_stream_words(L->bits, (int64_t)T * L->head_dim);
+  else
+    *code_bytes = BH * T * (uint64_t)kvqr_row_bytes(L->bits, L->head_dim);
   /* one binary16 zero + one binary16 step per (block, channel) */
   *stat_bytes = BH * (uint64_t)n_filled * (uint64_t)L->head_dim * 4u;
   return KVQR_OK;

@@ -70,6 +70,9 @@ int kvqr_validate(const kvqr_layout* L);
 int64_t kvqr_total_tokens(const kvqr_layout* L, int32_t n_filled);
 int64_t kvqr_block_offset(const kvqr_layout* L, int32_t block);
 int32_t kvqr_row_bytes(int32_t bits, int32_t head_dim);
+/* word-aligned layout (pack_mode 1): codes per 32-bit word, words of a stream */
+int32_t kvqr_codes_per_word(int32_t bits);
+int64_t kvqr_stream_words(int32_t bits, int64_t n_codes);
 
 /* one (block, channel) group: n values at x[i*stride] */
 int kvqr_quantize_group(const float* x, int64_t n, int64_t stride, int32_t bits,
@@ -80,7 +83,9 @@ int kvqr_quantize_block(const kvqr_layout* L, int32_t block, int32_t src_dtype,
                         const void* k_src, const void* v_src, kvqr_cache k_cache,
                         kvqr_cache v_cache);
 
-/* bit packing of rows of one-code-per-byte */
+/* bit packing of rows of one-code-per-byte.  pack_mode 0: each row LSB-first
+ * into ceil(bits*row_len/8) bytes at dst + r*stride.  pack_mode 1: all rows as
+ * one stream into 32-bit words of floor(32/bits) codes (stride must be 0). */
 void kvqr_pack_row(int32_t bits, const uint8_t* codes, int32_t n, uint8_t* out);
 void kvqr_unpack_row(int32_t bits, const uint8_t* in, int32_t n, uint8_t* codes);
 int kvqr_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,

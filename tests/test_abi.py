@@ -131,3 +131,29 @@ def test_quantize_attend_argument_errors_return_before_launch():
              None) == E
     L5 = K.make_layout(2, 3, 64, 5, (1, 4, 9))
     assert f(C.byref(L5), 0, *ok) == kb.E_UNSUPPORTED
+
+
+def test_word_aligned_mode_bytes_and_errors(oracle):
+    """pack_mode 1: byte accounting agrees with the oracle, the stream packer
+    rejects a row stride, and the decode calls report it unsupported."""
+    lib = K.lib()
+    for bits in (2, 3, 5, 8):
+        Lg = K.make_layout(3, 5, 64, bits, vi.VAR_BLOCKS, pack_mode=1)
+        Lo = oracle.make_layout(3, 5, 64, bits, vi.VAR_BLOCKS, pack_mode=1)
+        for n_filled in (0, 1, 7, 10):
+            assert K.kvq_bytes(Lg, n_filled) == oracle.nbytes(Lo, n_filled)
+    E = kb.E_INVAL
+    assert lib.kvq_pack(3, 1, FAKE, 4, 64, FAKE, 32, None) == E   # stream: stride must be 0
+    assert lib.kvq_unpack(3, 1, FAKE, 24, 4, 64, FAKE, None) == E
+    assert lib.kvq_pack(3, 2, FAKE, 4, 64, FAKE, 0, None) == E    # no pack_mode 2
+    assert lib.kvq_pack(3, 1, FAKE, 0, 64, None, 0, None) == kb.OK  # nothing to do
+    L = K.make_layout(2, 3, 64, 3, (1, 4, 9), pack_mode=1)
+    U = kb.E_UNSUPPORTED
+    assert lib.kvq_quantize_block(C.byref(L), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None,
+                                  None) == U
+    assert lib.kvq_attend_packed(C.byref(L), 0, FAKE, _cache(), _cache(), 0.0, FAKE, None) == U
+    assert lib.kvq_quantize_attend(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(), _cache(),
+                                   0.0, FAKE, None, None) == U
+    L.pack_mode = 2
+    with pytest.raises(K.KvqError):
+        K.kvq_bytes(L, 1)

@@ -189,3 +189,22 @@ def test_dequantize_matches_oracle(oracle, name):
         K.kvq_dequantize(Lg, n_filled, vg, out)
         ref = oracle.dequantize(Lo, n_filled, vo)
         assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("n_rows,row_len", [(1, 1), (5, 64), (37, 128), (680, 64)])
+def test_word_aligned_pack_matches_oracle(oracle, bits, n_rows, row_len):
+    """pack_mode 1 (one stream of 32-bit words, floor(32/bits) codes each):
+    bit-exact against the oracle, and unpack inverts it."""
+    rng = np.random.default_rng(100 * bits + n_rows)
+    codes = rng.integers(0, 1 << bits, size=(n_rows, row_len), dtype=np.uint8)
+    ref = oracle.pack(bits, codes, pack_mode=1)
+    dst = torch.full((ref.size + 16,), 0xA5, dtype=torch.uint8, device=DEV)
+    K.kvq_pack(bits, torch.from_numpy(codes).to(DEV), dst, pack_mode=1)
+    back = torch.zeros((n_rows, row_len), dtype=torch.uint8, device=DEV)
+    K.kvq_unpack(bits, dst, row_len, back, pack_mode=1)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:ref.size], ref)
+    assert (got[ref.size:] == 0xA5).all()  # nothing written past the last word
+    assert np.array_equal(back.cpu().numpy(), codes)

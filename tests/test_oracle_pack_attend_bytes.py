@@ -230,10 +230,11 @@ def test_bytes_reproduce_the_pages_int4_and_bf16_rows(oracle):
     assert seen == 6
 
 
-def test_bytes_dense_int3_and_the_tables_int3_reading(oracle):
+def test_bytes_dense_int3_and_the_tables_int3_rows(oracle):
     """Dense 3-bit rows give 78.31% on the VAR schedule; the table's INT3 rows
-    (77.06%) correspond to 3.2 stored bits per code (10 codes per 32-bit word).
-    Both figures are recorded; the dense layout is the one built."""
+    (77.06%, 3.81 / 5.48 / 8.57) are reproduced by the word-aligned layout
+    (pack_mode 1, 10 codes per 32-bit word).  The decode path keeps dense rows."""
+    seen = 0
     for m, layers, width, batch, method, prec, kv, saving in read_kv_table():
         if prec != "INT3":
             continue
@@ -244,9 +245,71 @@ def test_bytes_dense_int3_and_the_tables_int3_reading(oracle):
         dense = 2 * layers * (cb + sb) / GIB
         assert round(100 * (1 - dense / bf16), 2) == 78.31
         assert cb == seqs * (width // 64) * 680 * 24
-        word_aligned_bits = 3.2 + 32 * 10 / 680
-        assert round(100 * (1 - word_aligned_bits / 16), 2) == saving
-        assert round(bf16 * word_aligned_bits / 16, 2) == kv
+        Lw = oracle.make_layout(seqs, width // 64, 64, 3, vi.VAR_BLOCKS, pack_mode=1)
+        cw, sw = oracle.nbytes(Lw, 10)
+        assert sw == sb
+        assert cw == seqs * (width // 64) * 4 * ((680 * 64 + 9) // 10)
+        gib = 2 * layers * (cw + sw) / GIB
+        assert round(gib, 2) == kv, (m, gib)
+        assert round(100 * (1 - gib / bf16), 2) == saving
+        seen += 1
+    assert seen == 3
+
+
+def read_word_examples():
+    out = []
+    for line in open(os.path.join(GOLDEN, "pack_words_examples.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        bits, codes, packed = [x.strip() for x in line.split("|")]
+        out.append((int(bits), [int(c) for c in codes.split()], bytes.fromhex(packed)))
+    return out
+
+
+@pytest.mark.parametrize("bits,codes,expect", read_word_examples())
+def test_word_aligned_pack_worked_examples(oracle, bits, codes, expect):
+    c = np.array([codes], np.uint8)
+    got = oracle.pack(bits, c, pack_mode=1)
+    assert got.tobytes() == expect
+    assert np.array_equal(oracle.unpack(bits, got, len(codes), pack_mode=1, n_rows=1), c)
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_word_aligned_round_trip_and_size(oracle, bits):
+    rng = np.random.default_rng(bits)
+    for n_rows, row_len in [(1, 1), (3, 7), (5, 64), (17, 128)]:
+        codes = rng.integers(0, 1 << bits, size=(n_rows, row_len), dtype=np.uint8)
+        packed = oracle.pack(bits, codes, pack_mode=1)
+        cpw = 32 // bits
+        assert oracle.codes_per_word(bits) == cpw
+        assert packed.size == 4 * -(-n_rows * row_len // cpw)
+        assert np.array_equal(oracle.unpack(bits, packed, row_len, pack_mode=1, n_rows=n_rows), codes)
+        # spare top bits of every word are zero
+        words = packed.view("<u4")
+        if 32 % bits:
+            assert not (words >> (bits * cpw)).any()
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+def test_word_aligned_equals_dense_stream_when_words_fill(oracle, bits):
+    """When bits divides 32 the word layout is the dense LSB-first stream."""
+    rng = np.random.default_rng(10 + bits)
+    codes = rng.integers(0, 1 << bits, size=(4, 96), dtype=np.uint8)
+    words = oracle.pack(bits, codes, pack_mode=1)
+    dense = oracle.pack(bits, codes.reshape(1, -1))
+    assert words.tobytes() == dense.tobytes()
+
+
+def test_word_aligned_layout_rejected_on_the_decode_path(oracle):
+    wl = vi.Workload("w", 1, 1, 2, 64, 3, (4, 9), "bf16", seed=3)
+    L = oracle.make_layout(1, 2, 64, 3, (4, 9), pack_mode=1)
+    c = oracle.alloc_cache(oracle.make_layout(1, 2, 64, 3, (4, 9)))
+    assert oracle.quantize_block(L, 0, vi.kv_block(wl, 0, "k", 0), vi.kv_block(wl, 0, "v", 0),
+                                 c, c) == oracle.E_INVAL
+    L.pack_mode = 2
+    with pytest.raises(Exception):
+        oracle.nbytes(L, 1)
 
 
 def test_bytes_formula_pieces(oracle):

@@ -22,7 +22,7 @@ int validate_layout(const kvq_layout* L) {
   if (L->head_dim < 8 || L->head_dim % 8 != 0) return KVQ_E_INVAL;
   if (L->bits < 1 || L->bits > 8) return KVQ_E_INVAL;
   if (L->n_blocks < 1 || L->n_blocks > KVQ_MAX_BLOCKS) return KVQ_E_INVAL;
-  if (L->pack_mode != 0) return KVQ_E_INVAL;
+  if (L->pack_mode != 0 && L->pack_mode != 1) return KVQ_E_INVAL;
   int64_t T = 0;
   for (int i = 0; i < L->n_blocks; ++i) {
     if (L->block_tokens[i] < 1) return KVQ_E_INVAL;
@@ -37,6 +37,7 @@ int validate_layout(const kvq_layout* L) {
 
 // kernels are built for 3/4-bit codes and head_dim 64/128
 int gpu_supported(const kvq_layout* L) {
+  if (L->pack_mode != 0) return KVQ_E_UNSUPPORTED;  // the decode path keeps dense rows
   if (L->bits != 3 && L->bits != 4) return KVQ_E_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return KVQ_E_UNSUPPORTED;
   // one (b, h)'s rows are addressed with 32-bit buffer offsets
@@ -177,7 +178,13 @@ int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
     return KVQ_E_INVAL;
   const uint64_t bh = (uint64_t)layout->batch * (uint64_t)layout->heads;
   const uint64_t T = (uint64_t)offset_of(layout, n_filled);
-  *code_bytes = bh * T * (uint64_t)row_bytes(layout->bits, layout->head_dim);
+  if (layout->pack_mode == 1) {  // one word-aligned stream of T*D codes per (b, h)
+    const uint64_t cpw = 32u / (uint64_t)layout->bits;
+    const uint64_t n = T * (uint64_t)layout->head_dim;
+    *code_bytes = bh * 4u * ((n + cpw - 1) / cpw);
+  } else {
+    *code_bytes = bh * T * (uint64_t)row_bytes(layout->bits, layout->head_dim);
+  }
   *stat_bytes = bh * (uint64_t)n_filled * (uint64_t)layout->head_dim * 4u;
   return KVQ_OK;
 }
@@ -195,7 +202,15 @@ int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtyp
 
 int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,
              int32_t row_len, uint8_t* dst, int64_t dst_row_stride, hipStream_t stream) {
-  if (bits < 1 || bits > 8 || pack_mode != 0 || n_rows < 0 || row_len < 1) return KVQ_E_INVAL;
+  if (bits < 1 || bits > 8 || n_rows < 0 || row_len < 1) return KVQ_E_INVAL;
+  if (pack_mode == 1) {  // one word-aligned stream; no row stride
+    if (dst_row_stride != 0) return KVQ_E_INVAL;
+    if (n_rows == 0) return KVQ_OK;
+    if (!codes || !dst || !aligned16(codes) || !aligned16(dst)) return KVQ_E_INVAL;
+    if (n_rows > kMaxElems / row_len) return KVQ_E_INVAL;
+    return device_status(launch_pack_words(codes, dst, n_rows * row_len, bits, stream));
+  }
+  if (pack_mode != 0) return KVQ_E_INVAL;
   const int32_t R = row_bytes(bits, row_len);
   if (dst_row_stride < R) return KVQ_E_INVAL;
   if (n_rows == 0) return KVQ_OK;
@@ -218,7 +233,15 @@ int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_ro
 
 int kvq_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_row_stride,
                int64_t n_rows, int32_t row_len, uint8_t* codes, hipStream_t stream) {
-  if (bits < 1 || bits > 8 || pack_mode != 0 || n_rows < 0 || row_len < 1) return KVQ_E_INVAL;
+  if (bits < 1 || bits > 8 || n_rows < 0 || row_len < 1) return KVQ_E_INVAL;
+  if (pack_mode == 1) {
+    if (src_row_stride != 0) return KVQ_E_INVAL;
+    if (n_rows == 0) return KVQ_OK;
+    if (!codes || !src || !aligned16(codes) || !aligned16(src)) return KVQ_E_INVAL;
+    if (n_rows > kMaxElems / row_len) return KVQ_E_INVAL;
+    return device_status(launch_unpack_words(src, codes, n_rows * row_len, bits, stream));
+  }
+  if (pack_mode != 0) return KVQ_E_INVAL;
   if (src_row_stride < row_bytes(bits, row_len)) return KVQ_E_INVAL;
   if (n_rows == 0) return KVQ_OK;
   if (!codes || !src || !aligned16(codes) || !aligned16(src)) return KVQ_E_INVAL;

@@ -204,6 +204,11 @@ hipError_t launch_quantize(const QuantParams& p, int head_dim, int bits, bool f3
                            hipStream_t s);
 hipError_t launch_pack(const PackParams& p, hipStream_t s);
 hipError_t launch_unpack(const UnpackParams& p, hipStream_t s);
+// word-aligned stream of n codes (pack_mode 1)
+hipError_t launch_pack_words(const uint8_t* codes, uint8_t* dst, int64_t n, int bits,
+                             hipStream_t s);
+hipError_t launch_unpack_words(const uint8_t* src, uint8_t* codes, int64_t n, int bits,
+                               hipStream_t s);
 hipError_t launch_dequantize(const DequantParams& p, hipStream_t s);
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s);
 // quantize block k (q) then attend its queries (a): one launch where a fused

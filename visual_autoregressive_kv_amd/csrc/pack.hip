@@ -9,6 +9,8 @@
 // 128-bit stores, otherwise each chunk is written bytewise in place.
 #include "kvq_internal.h"
 
+#include <algorithm>
+
 namespace kvq {
 namespace {
 
@@ -125,6 +127,38 @@ __global__ __launch_bounds__(kWG) void stream_copy_kernel(const u32x4* __restric
 
 }  // namespace
 
+// Word-aligned stream (pack_mode 1): word w holds codes w*cpw .. w*cpw + cpw - 1
+// of the stream, cpw = floor(32 / bits), low bits first; one thread per word
+// reads its codes (one per byte) and writes one 32-bit word.
+__global__ __launch_bounds__(256) void pack_words_kernel(const uint8_t* __restrict__ codes,
+                                                         uint32_t* __restrict__ dst, int64_t n,
+                                                         int64_t words, int bits) {
+  const int cpw = 32 / bits;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i0 = w * cpw;
+    uint32_t word = 0;
+    for (int k = 0; k < cpw; ++k)
+      if (i0 + k < n) word |= ((uint32_t)codes[i0 + k] & mask) << (bits * k);
+    dst[w] = word;
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_words_kernel(const uint32_t* __restrict__ src,
+                                                           uint8_t* __restrict__ codes, int64_t n,
+                                                           int64_t words, int bits) {
+  const int cpw = 32 / bits;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t word = src[w];
+    const int64_t i0 = w * cpw;
+    for (int k = 0; k < cpw; ++k)
+      if (i0 + k < n) codes[i0 + k] = (uint8_t)((word >> (bits * k)) & mask);
+  }
+}
+
 hipError_t launch_pack(const PackParams& p, hipStream_t s) {
   if (p.n_chunks == 0) return hipSuccess;
   const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
@@ -143,6 +177,24 @@ hipError_t launch_dequantize(const DequantParams& p, hipStream_t s) {
   if (p.n_chunks == 0) return hipSuccess;
   const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_words(const uint8_t* codes, uint8_t* dst, int64_t n, int bits,
+                             hipStream_t s) {
+  const int64_t words = (n + 32 / bits - 1) / (32 / bits);
+  const int64_t grid = std::min<int64_t>((words + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_words_kernel, dim3((unsigned)grid), dim3(256), 0, s, codes,
+                     reinterpret_cast<uint32_t*>(dst), n, words, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_words(const uint8_t* src, uint8_t* codes, int64_t n, int bits,
+                               hipStream_t s) {
+  const int64_t words = (n + 32 / bits - 1) / (32 / bits);
+  const int64_t grid = std::min<int64_t>((words + 255) / 256, 65536);
+  hipLaunchKernelGGL(unpack_words_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(src), codes, n, words, bits);
   return hipGetLastError();
 }
 

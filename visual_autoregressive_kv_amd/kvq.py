@@ -194,23 +194,45 @@ def kvq_quantize_block(layout: Layout, block: int, k_src: torch.Tensor, v_src: t
                                     _cache(layout, v_cache, "v_cache"), sp, _stream(stream)))
 
 
-def kvq_pack(bits: int, codes: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
-    """codes: uint8 [n_rows, row_len]; dst: uint8 [n_rows, stride >= ceil(bits*row_len/8)]."""
-    if codes.dim() != 2 or dst.dim() != 2 or codes.shape[0] != dst.shape[0]:
-        raise ValueError("codes [n_rows, row_len] and dst [n_rows, stride] expected")
+def kvq_pack(bits: int, codes: torch.Tensor, dst: torch.Tensor, pack_mode: int = 0,
+             stream=None) -> None:
+    """codes: uint8 [n_rows, row_len].  pack_mode 0: dst uint8 [n_rows, stride >=
+    ceil(bits*row_len/8)]; pack_mode 1: dst uint8 [4 * words] (one word-aligned stream)."""
+    if codes.dim() != 2:
+        raise ValueError("codes [n_rows, row_len] expected")
     n_rows, row_len = codes.shape
-    _check("kvq_pack", lib().kvq_pack(bits, 0, _dev(codes, "codes", torch.uint8), n_rows, row_len,
-                                      _dev(dst, "dst", torch.uint8), dst.shape[1],
+    if pack_mode == 1:
+        words = -(-n_rows * row_len // (32 // bits))
+        if dst.dim() != 1 or dst.numel() < 4 * words:
+            raise ValueError("dst must be a 1-D uint8 tensor of 4 * words bytes")
+        stride = 0
+    else:
+        if dst.dim() != 2 or codes.shape[0] != dst.shape[0]:
+            raise ValueError("codes [n_rows, row_len] and dst [n_rows, stride] expected")
+        stride = dst.shape[1]
+    _check("kvq_pack", lib().kvq_pack(bits, pack_mode, _dev(codes, "codes", torch.uint8), n_rows,
+                                      row_len, _dev(dst, "dst", torch.uint8), stride,
                                       _stream(stream)))
 
 
 def kvq_unpack(bits: int, src: torch.Tensor, row_len: int, codes: torch.Tensor,
-               stream=None) -> None:
-    if src.dim() != 2 or tuple(codes.shape) != (src.shape[0], row_len):
-        raise ValueError("src [n_rows, stride] and codes [n_rows, row_len] expected")
-    _check("kvq_unpack", lib().kvq_unpack(bits, 0, _dev(src, "src", torch.uint8), src.shape[1],
-                                          src.shape[0], row_len,
-                                          _dev(codes, "codes", torch.uint8), _stream(stream)))
+               pack_mode: int = 0, stream=None) -> None:
+    """pack_mode 0: src [n_rows, stride]; pack_mode 1: src 1-D stream; codes [n_rows, row_len]."""
+    if codes.dim() != 2 or codes.shape[1] != row_len:
+        raise ValueError("codes [n_rows, row_len] expected")
+    n_rows = codes.shape[0]
+    if pack_mode == 1:
+        words = -(-n_rows * row_len // (32 // bits))
+        if src.dim() != 1 or src.numel() < 4 * words:
+            raise ValueError("src must be a 1-D uint8 tensor of 4 * words bytes")
+        stride = 0
+    else:
+        if src.dim() != 2 or src.shape[0] != n_rows:
+            raise ValueError("src [n_rows, stride] expected")
+        stride = src.shape[1]
+    _check("kvq_unpack", lib().kvq_unpack(bits, pack_mode, _dev(src, "src", torch.uint8), stride,
+                                          n_rows, row_len, _dev(codes, "codes", torch.uint8),
+                                          _stream(stream)))
 
 
 def kvq_dequantize(layout: Layout, n_filled: int, cache, out: torch.Tensor,
