@@ -136,10 +136,12 @@ def test_reads_only_the_prefix(oracle):
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
-@pytest.mark.parametrize("blocks", [(2,) * 16, (1,) * 40 + (3,), (5, 1, 30, 31, 64)])
+@pytest.mark.parametrize("blocks", [(2,) * 16, (1,) * 40 + (3,), (5, 1, 30, 31, 64),
+                                    (1,) * 63 + (70,)])
 def test_many_short_blocks(oracle, head_dim, blocks):
     """Short blocks whose statistics do or do not fit the per-wave LDS staging of
-    the short-block kernel (16 vs 41 blocks), and 30/31/64-query blocks."""
+    the short-block kernel (16 vs 41 blocks), 30/31/64-query blocks, and the
+    64-block maximum (64 KB of staged statistics at head_dim 128)."""
     wl = vi.Workload("short", 1, 2, 5, head_dim, 4 if head_dim == 64 else 3, blocks, "bf16",
                      rope=False, seed=5)
     Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)

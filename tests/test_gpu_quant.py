@@ -45,8 +45,18 @@ def test_full_batch_block(oracle, name, block):
 
 
 def test_video_frames_two_pass_path(oracle):
-    """D=128, 1560-token frames: tiles too large for registers take two passes."""
+    """D=128, 1560-token frames at batch 1 (80 tiles): the token-sliced path."""
     wl = vi.WORKLOADS["video_16x1560_h40d128_int3"].with_(blocks=(1560, 1560, 1560))
+    _, _, kg, vg, ko, vo = fill_both(oracle, wl)
+    assert_cache_equal(kg, ko, "K")
+    assert_cache_equal(vg, vo, "V")
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_large_blocks_many_tiles(oracle, bits):
+    """Blocks too large for registers with at least 1024 (tensor, b, h) tiles:
+    one workgroup per tile streams it twice."""
+    wl = vi.Workload("many", 1, 13, 40, 128, bits, (3, 200), "bf16", seed=11)
     _, _, kg, vg, ko, vo = fill_both(oracle, wl)
     assert_cache_equal(kg, ko, "K")
     assert_cache_equal(vg, vo, "V")
@@ -67,8 +77,10 @@ def test_ragged_edge_shapes(oracle, bits, src, head_dim):
 
 
 def test_writes_stay_inside_the_block(oracle):
-    """Canary bytes: only rows [off_k, off_k + n_k) and stats slot k change."""
-    wl = vi.Workload("canary", 1, 3, 5, 64, 3, (1, 4, 9, 16, 25, 36), "bf16", seed=3)
+    """Canary bytes: only rows [off_k, off_k + n_k) and stats slot k change
+    (the 300-token block takes the token-sliced path, which parks its slice
+    extremes in the block's own rows)."""
+    wl = vi.Workload("canary", 1, 3, 5, 64, 3, (1, 4, 9, 16, 25, 36, 300), "bf16", seed=3)
     Lg, Lo = layouts(oracle, wl)
     for block in range(len(wl.blocks)):
         kg, vg = K.alloc_cache(Lg), K.alloc_cache(Lg)
@@ -108,8 +120,11 @@ def test_deterministic(oracle):
 
 
 @pytest.mark.parametrize("src", ["bf16", "f32"])
-def test_status_flags(oracle, src):
-    wl = vi.Workload("status", 1, 2, 3, 64, 4, (16, 16), src, seed=5)
+@pytest.mark.parametrize("n,row", [(16, 2), (300, 290)])
+def test_status_flags(oracle, src, n, row):
+    """Screened quantization: NaN/Inf and out-of-binary16-range inputs set their
+    flags; one register pass (16 tokens) and the token-sliced path (300)."""
+    wl = vi.Workload("status", 1, 2, 3, 64, 4, (16, n), src, seed=5)
     Lg, _ = layouts(oracle, wl)
     kb = vi.kv_block(wl, 0, "k", 1)
     vb = vi.kv_block(wl, 0, "v", 1)
@@ -131,9 +146,9 @@ def test_status_flags(oracle, src):
     def put(arr, val):
         a = arr.copy()
         if src == "f32":
-            a[1, 3, 2, 17] = np.float32(val)
+            a[1, row, 2, 17] = np.float32(val)
         else:
-            a[1, 3, 2, 17] = vi.f32_to_bf16_bits(np.array([val], np.float32))[0]
+            a[1, row, 2, 17] = vi.f32_to_bf16_bits(np.array([val], np.float32))[0]
         return a
 
     for val, flag in [(np.nan, K.S_NONFINITE), (np.inf, K.S_NONFINITE),

@@ -19,7 +19,13 @@
 //      each 8 straddle bytes and a block's rows may start 8 bytes off a
 //      16-byte boundary) and written with coalesced 128-bit stores, never
 //      touching bytes outside the block's rows.
-// Tiles too large for registers (video frames) take two passes over HBM.
+// Tiles too large for registers (video frames) take two passes over HBM:
+//   - many tiles: one workgroup per tile streams it twice (extremes, codes);
+//   - few tiles (a batch of one video sequence has 2 x heads of them): every
+//     tile is cut into register-sized token slices, one workgroup each, over
+//     three launches: slice extremes (parked in the block's own code rows,
+//     which the last launch overwrites), per-tile statistics, slice codes.
+//     Min/max merge in any order, so the bytes are those of one pass.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -92,6 +98,66 @@ __device__ __forceinline__ int nonfinite(const Chunk<F32>& c) {
   return bad;
 }
 
+// Per-thread extremes of the rows [row_base + i * rps] (i < nvalid) of 8 channels.
+template <bool F32, bool CHECK>
+__device__ __forceinline__ void extremes8(const Chunk<F32> (&v)[kMaxRpt], int nvalid, float (&mn)[8],
+                                          float (&mx)[8], int& bad) {
+#pragma unroll
+  for (int i = 0; i < kMaxRpt; i += 2) {
+    if (i < nvalid) {
+      const int i2 = (i + 1 < nvalid) ? i + 1 : i;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float a = chan_order<F32>(v[i], j);
+        const float c = chan_order<F32>(v[i2], j);
+        mn[j] = min3f(mn[j], a, c);
+        mx[j] = max3f(mx[j], a, c);
+      }
+      if constexpr (CHECK) bad |= nonfinite<F32>(v[i]) | nonfinite<F32>(v[i2]);
+    }
+  }
+}
+
+// Codes of the register rows of one pass, staged in LDS with the destination's
+// 16-byte misalignment, then written with 128-bit stores plus byte-exact head
+// and tail.  Every thread of the workgroup calls it (one barrier inside).
+template <int D, int BITS, bool F32>
+__device__ __forceinline__ void pack_store(const Chunk<F32> (&v)[kMaxRpt], int nvalid, int r0, int rps,
+                                           int cg, const float (&zf)[8], const float (&inv)[8],
+                                           uint8_t* my_stage, uint8_t* dst, int rows_here, int R,
+                                           int lt, int gs) {
+  constexpr int CPR = D / 8;
+  const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
+#pragma unroll
+  for (int i = 0; i < kMaxRpt; ++i) {
+    if (i < nvalid) {
+      float xv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = chan<F32>(v[i], j);
+      const uint32_t acc = pack_codes8<BITS>(xv, zf, inv);
+      const int chunk = (r0 + i * rps) * CPR + cg;  // within this pass
+      uint8_t* sp = my_stage + mis + chunk * BITS;
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<uint32_t*>(sp) = acc;
+      } else {
+        sp[0] = (uint8_t)acc;
+        sp[1] = (uint8_t)(acc >> 8);
+        sp[2] = (uint8_t)(acc >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  const int nbytes = rows_here * R;
+  const int head = min((16 - mis) & 15, nbytes);
+  const int body = (nbytes - head) >> 4;
+  const int tail = nbytes - head - (body << 4);
+  const uint8_t* sp = my_stage + mis;
+  for (int k = lt; k < body; k += gs)
+    *reinterpret_cast<u32x4*>(dst + head + 16 * k) = *reinterpret_cast<const u32x4*>(sp + head + 16 * k);
+  if (lt < head) dst[lt] = sp[lt];
+  if (lt < tail) dst[head + 16 * body + lt] = sp[head + 16 * body + lt];
+}
+
 template <int D, int BITS, bool F32, bool CHECK, bool STREAM>
 __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
   constexpr int CPR = D / 8;  // 8-channel chunks per row
@@ -140,20 +206,7 @@ __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
 #pragma unroll
     for (int i = 0; i < kMaxRpt; ++i)
       if (i < nvalid) load_chunk<F32>(v[i], src, base + (int64_t)(row_base + i * rps) * row_stride);
-#pragma unroll
-    for (int i = 0; i < kMaxRpt; i += 2) {
-      if (i < nvalid) {
-        const int i2 = (i + 1 < nvalid) ? i + 1 : i;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float a = chan_order<F32>(v[i], j);
-          const float c = chan_order<F32>(v[i2], j);
-          mn[j] = min3f(mn[j], a, c);
-          mx[j] = max3f(mx[j], a, c);
-        }
-        if constexpr (CHECK) bad |= nonfinite<F32>(v[i]) | nonfinite<F32>(v[i2]);
-      }
-    }
+    extremes8<F32, CHECK>(v, nvalid, mn, mx, bad);
   }
 
   // ---- phase 2: reduce across the tile's threads ---------------------------
@@ -237,39 +290,176 @@ __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
           load_chunk<F32>(v[i], src, base + (int64_t)(row_base + i * rps) * row_stride);
     }
     uint8_t* dst = dst_tile + (int64_t)pass_row0 * p.R;
-    const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
-#pragma unroll
-    for (int i = 0; i < kMaxRpt; ++i) {
-      if (i < nvalid) {
-        float xv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = chan<F32>(v[i], j);
-        const uint32_t acc = pack_codes8<BITS>(xv, zf, inv);
-        const int chunk = (r0 + i * rps) * CPR + cg;  // within this pass
-        uint8_t* sp = my_stage + mis + chunk * BITS;
-        if constexpr (BITS == 4) {
-          *reinterpret_cast<uint32_t*>(sp) = acc;
-        } else {
-          sp[0] = (uint8_t)acc;
-          sp[1] = (uint8_t)(acc >> 8);
-          sp[2] = (uint8_t)(acc >> 16);
-        }
-      }
-    }
-    __syncthreads();
     const int rows_here = max(0, min(n - pass_row0, rows_per_pass));
-    const int nbytes = rows_here * p.R;
-    const int head = min((16 - mis) & 15, nbytes);
-    const int body = (nbytes - head) >> 4;
-    const int tail = nbytes - head - (body << 4);
-    const uint8_t* sp = my_stage + mis;
-    for (int k = lt; k < body; k += gs)
-      *reinterpret_cast<u32x4*>(dst + head + 16 * k) =
-          *reinterpret_cast<const u32x4*>(sp + head + 16 * k);
-    if (lt < head) dst[lt] = sp[lt];
-    if (lt < tail) dst[head + 16 * body + lt] = sp[head + 16 * body + lt];
+    pack_store<D, BITS, F32>(v, nvalid, r0, rps, cg, zf, inv, my_stage, dst, rows_here, p.R, lt, gs);
     if constexpr (STREAM) __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Token-sliced path (few large tiles).  A slice is one register pass of a
+// 256-thread workgroup: kSliceRows(D) rows.  Slice s of a tile parks its 2 x D
+// float extremes at float offset 2 D s of the tile's block rows (n_k * R bytes,
+// at least 8 D bytes per slice for every supported width, checked by the host).
+// ---------------------------------------------------------------------------
+template <int D>
+constexpr int kSliceRows = (kWG / (D / 8)) * kMaxRpt;
+
+__device__ __forceinline__ void tile_of(const QuantParams& p, int64_t tile, int& kv, int& bh, int& b,
+                                        int& h) {
+  kv = (int)(tile / p.BH);
+  bh = (int)(tile - (int64_t)kv * p.BH);
+  b = bh / p.H;
+  h = bh - b * p.H;
+}
+
+// load this thread's rows of slice `slice` of a tile into registers
+template <int D, bool F32>
+__device__ __forceinline__ int load_slice(const QuantParams& p, int kv, int b, int h, int slice,
+                                          int tid, Chunk<F32> (&v)[kMaxRpt]) {
+  constexpr int CPR = D / 8;
+  constexpr int rps = kWG / CPR;
+  const int cg = tid % CPR;
+  const int row_base = slice * kSliceRows<D> + tid / CPR;
+  const int64_t row_stride = (int64_t)p.H * D;
+  const int64_t base = ((int64_t)b * p.n * p.H + h) * D + 8 * cg;
+  int nvalid = 0;
+  if (row_base < p.n) nvalid = min(kMaxRpt, (p.n - row_base + rps - 1) / rps);
+#pragma unroll
+  for (int i = 0; i < kMaxRpt; ++i)
+    if (i < nvalid) load_chunk<F32>(v[i], p.src[kv], base + (int64_t)(row_base + i * rps) * row_stride);
+  return nvalid;
+}
+
+template <int D, bool F32, bool CHECK>
+__global__ __launch_bounds__(kWG) void slice_extremes_kernel(QuantParams p, int n_slices) {
+  constexpr int CPR = D / 8;
+  __shared__ float red_mn[kWG / kWave][CPR][8];
+  __shared__ float red_mx[kWG / kWave][CPR][8];
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x / n_slices;
+  const int slice = (int)(blockIdx.x - tile * n_slices);
+  int kv, bh, b, h;
+  tile_of(p, tile, kv, bh, b, h);
+  Chunk<F32> v[kMaxRpt];
+  const int nvalid = load_slice<D, F32>(p, kv, b, h, slice, tid, v);
+  float mn[8], mx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mn[j] = __uint_as_float(0x7F800000u);
+    mx[j] = __uint_as_float(0xFF800000u);
+  }
+  int bad = 0;
+  extremes8<F32, CHECK>(v, nvalid, mn, mx, bad);
+  for (int m = CPR; m < kWave; m <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
+      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
+    }
+  }
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  if (lane < CPR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      red_mn[wave][lane][j] = mn[j];
+      red_mx[wave][lane][j] = mx[j];
+    }
+  }
+  __syncthreads();
+  if (tid < CPR) {
+    float* ext = reinterpret_cast<float*>(p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R) +
+                 (int64_t)slice * 2 * D;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float lo = red_mn[0][tid][j], hi = red_mx[0][tid][j];
+      for (int w = 1; w < kWG / kWave; ++w) {
+        lo = fminf(lo, red_mn[w][tid][j]);
+        hi = fmaxf(hi, red_mx[w][tid][j]);
+      }
+      ext[8 * tid + j] = lo;
+      ext[D + 8 * tid + j] = hi;
+    }
+  }
+  if constexpr (CHECK) {
+    if (bad) atomicOr(p.status, KVQ_S_NONFINITE);
+  }
+}
+
+// one workgroup per tile, thread = channel: merge the slices, statistics
+template <int D, int BITS, bool F32, bool CHECK>
+__global__ __launch_bounds__(D) void slice_stats_kernel(QuantParams p, int n_slices) {
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  const int ch = threadIdx.x;
+  int kv, bh, b, h;
+  tile_of(p, blockIdx.x, kv, bh, b, h);
+  const float* ext = reinterpret_cast<const float*>(p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R);
+  float lo = __uint_as_float(0x7F800000u), hi = __uint_as_float(0xFF800000u);
+  for (int sl = 0; sl < n_slices; ++sl) {
+    lo = fminf(lo, ext[(int64_t)sl * 2 * D + ch]);
+    hi = fmaxf(hi, ext[(int64_t)sl * 2 * D + D + ch]);
+  }
+  if (!F32 && (ch & 1)) {  // drop the neighbouring channel's bits (ordering keys)
+    lo = __uint_as_float(__float_as_uint(lo) & 0xFFFF0000u);
+    hi = __uint_as_float(__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  int flags = 0;
+  const GroupStats g = group_stats<CHECK>(lo, hi, LEVELS, flags);
+  const int64_t so = (((int64_t)b * p.H + h) * p.NB + p.block) * D + ch;
+  p.zero[kv][so] = g.zb;
+  p.scale[kv][so] = g.sb;
+  if constexpr (CHECK) {
+    if (flags) atomicOr(p.status, flags);
+  }
+}
+
+// codes of one slice from the tile's binary16 statistics (zero and reciprocal
+// step rebuilt exactly as group_stats makes them)
+template <int D, int BITS, bool F32>
+__global__ __launch_bounds__(kWG) void slice_pack_kernel(QuantParams p, int n_slices) {
+  constexpr int CPR = D / 8;
+  __shared__ __align__(16) uint8_t stage[kStageBytes];
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x / n_slices;
+  const int slice = (int)(blockIdx.x - tile * n_slices);
+  int kv, bh, b, h;
+  tile_of(p, tile, kv, bh, b, h);
+  Chunk<F32> v[kMaxRpt];
+  const int nvalid = load_slice<D, F32>(p, kv, b, h, slice, tid, v);
+  const int cg = tid % CPR;
+  const int64_t so = (((int64_t)b * p.H + h) * p.NB + p.block) * D + 8 * cg;
+  const u32x4 zw = *reinterpret_cast<const u32x4*>(p.zero[kv] + so);
+  const u32x4 sw = *reinterpret_cast<const u32x4*>(p.scale[kv] + so);
+  float zf[8], inv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t zpair = word_of(zw, j >> 1), spair = word_of(sw, j >> 1);
+    zf[j] = h2f((uint16_t)((j & 1) ? (zpair >> 16) : (zpair & 0xFFFFu)));
+    const float sf = h2f((uint16_t)((j & 1) ? (spair >> 16) : (spair & 0xFFFFu)));
+    inv[j] = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+  }
+  const int row0 = slice * kSliceRows<D>;
+  uint8_t* dst = p.codes[kv] + ((int64_t)bh * p.T + p.off + row0) * p.R;
+  const int rows_here = min(p.n - row0, kSliceRows<D>);
+  pack_store<D, BITS, F32>(v, nvalid, tid / CPR, kWG / CPR, cg, zf, inv, stage, dst, rows_here, p.R,
+                           tid, kWG);
+}
+
+// tiles below which a block too large for registers is cut into slices
+constexpr int64_t kSliceTiles = 1024;
+
+template <int D, int BITS, bool F32, bool CHECK>
+hipError_t launch_sliced(const QuantParams& p, hipStream_t s) {
+  const int n_slices = (p.n + kSliceRows<D> - 1) / kSliceRows<D>;
+  // parked extremes must fit the block's rows
+  if ((int64_t)n_slices * 8 * D > (int64_t)p.n * p.R) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.n_tiles * n_slices));
+  hipLaunchKernelGGL((slice_extremes_kernel<D, F32, CHECK>), grid, dim3(kWG), 0, s, p, n_slices);
+  hipLaunchKernelGGL((slice_stats_kernel<D, BITS, F32, CHECK>), dim3((unsigned)p.n_tiles), dim3(D), 0,
+                     s, p, n_slices);
+  hipLaunchKernelGGL((slice_pack_kernel<D, BITS, F32>), grid, dim3(kWG), 0, s, p, n_slices);
+  return hipGetLastError();
 }
 
 template <int D, int BITS, bool F32>
@@ -278,6 +468,8 @@ hipError_t launch_t(const QuantParams& p, hipStream_t s) {
   const int64_t grid = (p.n_tiles + tiles_per_wg - 1) / tiles_per_wg;
   const bool stream = (int64_t)(p.gs / (D / 8)) * p.rpt < p.n;
   const bool check = p.status != nullptr;
+  if (stream && p.n_tiles < kSliceTiles)
+    return check ? launch_sliced<D, BITS, F32, true>(p, s) : launch_sliced<D, BITS, F32, false>(p, s);
   dim3 g((unsigned)grid), blk(kWG);
   if (check) {
     if (stream)
