@@ -396,6 +396,7 @@ __global__ __launch_bounds__(D) void slice_stats_kernel(QuantParams p, int n_sli
   tile_of(p, blockIdx.x, kv, bh, b, h);
   const float* ext = reinterpret_cast<const float*>(p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R);
   float lo = __uint_as_float(0x7F800000u), hi = __uint_as_float(0xFF800000u);
+#pragma unroll 8
   for (int sl = 0; sl < n_slices; ++sl) {
     lo = fminf(lo, ext[(int64_t)sl * 2 * D + ch]);
     hi = fmaxf(hi, ext[(int64_t)sl * 2 * D + D + ch]);
