@@ -7,18 +7,21 @@ scale k of the 10-scale VAR schedule and every layer, quantize + bit-pack the
 freshly decoded block's K and V into that layer's packed cache, then run
 block-causal attention of the block's queries over the packed cache, both in
 one launch (kvq_quantize_attend; head_dim 64, blocks of up to 256 tokens);
---unfused calls kvq_quantize_block then kvq_attend_packed for every block.  Inputs (K, V, Q of every block of every
-layer, bf16, synthetic VAR-shaped data drawn on the device) and caches are
+--unfused calls kvq_quantize_block then kvq_attend_packed for every block.
+Inputs (K, V, Q of every block of every layer, bf16, synthetic VAR-shaped
+data drawn on the device) and caches are
 resident in HBM before the timed region; every layer has its own buffers, so
 the 256 MB last-level cache cannot serve repeats.
 
 Printed: one JSON line.  `value` is packed-KV attention tokens/s over the whole
-step (query tokens x layers per second, quantize+pack included); per-kernel
-figures (`kernels`, `per_block_us`) come from HIP events recorded at every
-launch boundary on the launch stream during the timed steps; `roofline` is for
-the kernel kind with the largest share of the step, over the launches of that
-kind (`blocks`); `cpu_baseline` is the CPU oracle timed on a bounded sample of
-the same workload on the host's cores.
+step (query tokens x layers per second, quantize+pack included).  Per-kernel
+figures (`kernels`) come from HIP events on the launch stream over the timed
+steps: when every launch is of one kind (the fused VAR step) one event pair per
+step, otherwise events at every launch boundary; `per_block_us` are per-launch
+event spans (from a separate pass after the timed steps in the one-kind case).
+`roofline` is for the kernel kind with the largest share of the step, over the
+launches of that kind (`blocks`); `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload on the host's cores.
 """
 from __future__ import annotations
 
@@ -276,14 +279,38 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
-           for _ in range(args.steps)]
+    # Timed region.  When every launch of a step is of one kind (the fused VAR
+    # decode step), one event pair per step gives that kind's average launch
+    # duration (the spans of its launches tile the step), so nothing but the
+    # library calls runs between the events.  With several kinds, events mark
+    # every launch boundary.  Per-block spans then come from a separate pass
+    # after the timed region.
+    single_kind = len({c[0] for c in calls}) == 1
+
+    def new_events(k):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(args.steps)]
+
+    evs = new_events(2 if single_kind else n_calls + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):
-        step(evs[s_])
+        if single_kind:
+            evs[s_][0].record(stream)
+            step()
+            evs[s_][1].record(stream)
+        else:
+            step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # per-launch spans: the timed events (several kinds) or a separate pass
+    if single_kind:
+        span_evs = new_events(n_calls + 1)
+        for s_ in range(args.steps):
+            step(span_evs[s_])
+        torch.cuda.synchronize()
+    else:
+        span_evs = evs
 
     # per kind: summed event time, launches, algorithmic bytes and flops
     byte_model = {"quant_pack": quant_bytes, "attend": attend_bytes,
@@ -291,7 +318,7 @@ def main():
     kinds = {}
     per_block = {}
     for c, (kind, j, _, _) in enumerate(calls):
-        ms = sum(evs[s_][c].elapsed_time(evs[s_][c + 1]) for s_ in range(args.steps))
+        ms = sum(span_evs[s_][c].elapsed_time(span_evs[s_][c + 1]) for s_ in range(args.steps))
         k = kinds.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
         k["ms"] += ms
         k["launches"] += args.steps
@@ -299,6 +326,9 @@ def main():
         if kind in ("attend", "fused"):
             k["flops"] += attend_flops(wl, j) * args.steps
         per_block.setdefault(kind, {}).setdefault(j, []).append(ms / args.steps)
+    if single_kind:  # the kind's time is the timed steps' span
+        only = kinds[calls[0][0]]
+        only["ms"] = sum(e[0].elapsed_time(e[1]) for e in evs)
     per_block_us = {kind: [round(1e3 * sum(v) / len(v), 2) for _, v in sorted(d.items())]
                     for kind, d in per_block.items()}
     per_block_blocks = {kind: sorted(d) for kind, d in per_block.items()}
@@ -343,6 +373,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "kernels": kind_stats,
         "copy_peak_GBps": round(copy_gbps, 1),
+        "timing": ("one event pair per timed step; per-block spans from a separate pass"
+                   if single_kind else "events at every launch boundary of the timed steps"),
         "per_block_us": per_block_us,
         "roofline": roofline,
     }
