@@ -176,9 +176,9 @@ def cpu_baseline(wl, target_s: float):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build's path runs on a single MI355X "
-              "(it shards across GPUs with no exchange by batch or heads, which is not "
-              "built here); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the packed-KV path runs on a single MI355X "
+              "(it would shard across GPUs by batch or heads with no exchange; that "
+              "sharding is not implemented); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
