@@ -418,12 +418,12 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         const uint64_t v = (uint64_t)pre[i] | ((uint64_t)pre2[i] << 32);
         w = (uint32_t)(v >> s_shift[i]);
       }
+      // keys past the prefix read codes 0 (buffer range check) and keep the
+      // last block's statistics: finite values whose scores are masked out
       float cf[8], x[8];
       codes_f32<BITS>(w, cf);
-      const bool live = t < n_prefix;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        x[c] = live ? __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]) : 0.0f;
+      for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]);
       if (s_tensor[i] == 0) {
         u32x4 hi, lo;
 #pragma unroll
@@ -855,7 +855,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
       vc[i][1] = BITS != 4 ? vpre[i][1] : 0u;
     }
     if (j + 1 < n_tiles) issue_loads(j + 1);
-    const int tk = t0 + col;  // this lane's key
+    // this lane's key; past the prefix its codes read 0 and dequantize to
+    // finite values under the last block's statistics, masked in the scores
+    const int tk = t0 + col;
     const bool live = tk < n_prefix;
     if constexpr (FUSE != 0) {
       const int r = tk - (int)p.fz.off;  // row within block k
@@ -891,7 +893,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
       float cf[8], x[8];
       codes_f32<BITS>(bits_of(vc[i], v_shift[i]), cf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = live ? __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]) : 0.0f;
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
       const uint32_t h01 = pk_f16(x[0], x[1]), h23 = pk_f16(x[2], x[3]);
       const uint32_t h45 = pk_f16(x[4], x[5]), h67 = pk_f16(x[6], x[7]);
       const bool odd = v_key[i] & 1;
@@ -920,7 +922,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
         float cf[8], x[8];
         codes_f32<BITS>(bits_of(kc[ks], k_shift[ks]), cf);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]) : 0.0f;
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
         u32x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
