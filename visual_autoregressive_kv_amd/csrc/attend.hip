@@ -114,26 +114,6 @@ __device__ __forceinline__ void codes_f32(uint32_t w, float c[8]) {
   }
 }
 
-// the 8 codes of one packed chunk as binary16 pairs (c_j, c_j+4), j = 0..3,
-// biased by 1024 (binary16 1024 + c is exact; subtracting 1024 recovers c)
-template <int BITS>
-__device__ __forceinline__ void code_pairs_biased(uint32_t w, uint32_t cp[4]) {
-  // binary16 1024.0 in both halves, held in a vector register so that mask
-  // and bias fold into one v_and_or_b32 (which takes no literal operand)
-  uint32_t M;
-  asm("v_mov_b32 %0, 0x64006400" : "=v"(M));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (BITS == 4) {
-      cp[j] = ((w >> (4 * j)) & 0x000F000Fu) | M;  // nibbles j and j + 4
-    } else {
-      const uint32_t lo = (w >> (BITS * j)) & ((1u << BITS) - 1u);
-      const uint32_t hi = (w >> (BITS * (j + 4))) & ((1u << BITS) - 1u);
-      cp[j] = lo | (hi << 16) | M;
-    }
-  }
-}
-
 // Raw buffer view of key tile j of one (b, h)'s packed prefix.  The hardware
 // range check covers the per-lane offset only (not the scalar offset), so the
 // tile's start goes into the base address and the record count is what is
@@ -408,37 +388,14 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     }
   };
 
-  // V items of the 8-wave kernel (one item per thread) take the packed
-  // binary16 route below; the smaller kernels, with 2-4 items per thread,
-  // keep the fp32 route (the packed one's extra per-item state spills there)
-  constexpr bool PKV = NW == 8;
-  // per-slot cache of the current block's statistics; packed-route V slots
-  // keep them as channel pairs (j, j + 4) in dword j, the order of
-  // code_pairs_biased
+  // per-slot cache of the current block's statistics
   int s_blk[MAXI], s_next[MAXI];
   f16x8 s_z[MAXI], s_s[MAXI];
-  // (element shuffles only: extracting a dword from a bit-cast binary16
-  // vector is miscompiled by this compiler, which reads dword 0 for every one)
-  auto pair_j_j4 = [](f16x8 v) { return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7); };
-  auto load_item_stats = [&](int i, int blk) {
-    load_stats(blk, s_tensor[i], s_cg[i], s_z[i], s_s[i]);
-    if (PKV && s_tensor[i] != 0) {
-      s_z[i] = pair_j_j4(s_z[i]);
-      s_s[i] = pair_j_j4(s_s[i]);
-    }
-  };
-  // V slots: byte selectors of the key-pair exchange (even-key lanes write
-  // channels 0-3 of keys (2m, 2m+1), odd-key lanes channels 4-7)
-  uint32_t sel_send[MAXI], sel_a[MAXI], sel_b[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     s_blk[i] = 0;
     s_next[i] = blk_end[0];
-    load_item_stats(i, 0);
-    const bool odd = s_key[i] & 1;
-    sel_send[i] = odd ? 0x05040100u : 0x07060302u;  // low halves (ch 0-3) : high (4-7)
-    sel_a[i] = odd ? 0x03020504u : 0x05040100u;
-    sel_b[i] = odd ? 0x03020706u : 0x07060100u;
+    load_stats(0, s_tensor[i], s_cg[i], s_z[i], s_s[i]);
   }
 
   auto dequant = [&](int j, int buf) {
@@ -452,7 +409,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
           ++s_blk[i];
           s_next[i] = blk_end[s_blk[i]];
         } while (t >= s_next[i]);
-        load_item_stats(i, s_blk[i]);
+        load_stats(s_blk[i], s_tensor[i], cg, s_z[i], s_s[i]);
       }
       uint32_t w;
       if constexpr (BITS == 4) {
@@ -463,17 +420,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       }
       // keys past the prefix read codes 0 (buffer range check) and keep the
       // last block's statistics: finite values whose scores are masked out
-      // fp32 route: k_hat (and, in the smaller kernels, v_hat) = fma(code, s, z)
-      float x[8];
-      auto dequant_f32 = [&]() {
-        float cf[8];
-        codes_f32<BITS>(w, cf);
+      float cf[8], x[8];
+      codes_f32<BITS>(w, cf);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]);
-      };
-      if constexpr (!PKV) dequant_f32();
+      for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]);
       if (s_tensor[i] == 0) {
-        if constexpr (PKV) dequant_f32();
         u32x4 hi, lo;
 #pragma unroll
         for (int c = 0; c < 8; c += 2) {
@@ -485,35 +436,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         }
         *reinterpret_cast<u32x4*>(&k_hi[buf][s_key[i]][8 * cg]) = hi;
         *reinterpret_cast<u32x4*>(&k_lo[buf][s_key[i]][8 * cg]) = lo;
-      } else if constexpr (PKV) {
-        // v_hat of this key for channels (j, j + 4) in one binary16 pair:
-        // fma(code, s, z) rounded once (packed binary16 FMA)
-        uint32_t cp[4], r[4];
-        code_pairs_biased<BITS>(w, cp);
-        const f16x2 bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f16x2 code = __builtin_bit_cast(f16x2, cp[jj]) + bias;  // exact
-          const f16x2 sp = {s_s[i][2 * jj], s_s[i][2 * jj + 1]};      // (s_jj, s_jj+4)
-          const f16x2 zp = {s_z[i][2 * jj], s_z[i][2 * jj + 1]};
-          r[jj] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(code, sp, zp));
-        }
-        // the even-key lane writes channels 0-3 and the odd-key lane channels
-        // 4-7, as (key 2m, key 2m+1) pairs: each lane sends the four values
-        // its neighbour writes and merges the four it receives with its own
-        const bool odd = s_key[i] & 1;
-        const uint32_t q0 = swap_adjacent(__builtin_amdgcn_perm(r[1], r[0], sel_send[i]));
-        const uint32_t q1 = swap_adjacent(__builtin_amdgcn_perm(r[3], r[2], sel_send[i]));
-        const int d0 = 8 * cg + (odd ? 4 : 0);
-        uint32_t* vrow = &v_t[buf][d0][s_key[i] >> 1];
-        vrow[0 * VROW] = __builtin_amdgcn_perm(q0, r[0], sel_a[i]);  // channel d0
-        vrow[1 * VROW] = __builtin_amdgcn_perm(q0, r[1], sel_b[i]);  // d0 + 1
-        vrow[2 * VROW] = __builtin_amdgcn_perm(q1, r[2], sel_a[i]);  // d0 + 2
-        vrow[3 * VROW] = __builtin_amdgcn_perm(q1, r[3], sel_b[i]);  // d0 + 3
       } else {
-        // fp32 route: channel pairs of this key as fp16; the even-key lane
-        // writes channels 0-3 and the odd-key lane channels 4-7, each as
-        // (even, odd) key pairs
+        // channel pairs of this key as fp16; the even-key lane writes channels
+        // 0-3 and the odd-key lane channels 4-7, each as (even, odd) key pairs
         const uint32_t h01 = pk_f16(x[0], x[1]), h23 = pk_f16(x[2], x[3]);
         const uint32_t h45 = pk_f16(x[4], x[5]), h67 = pk_f16(x[6], x[7]);
         const bool odd = s_key[i] & 1;
