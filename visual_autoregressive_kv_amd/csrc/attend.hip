@@ -4,15 +4,17 @@
 // to every cached token of blocks 0..k.  One workgroup owns up to 256 queries of
 // one (sequence, head); its waves own 32 queries each.  The packed prefix is
 // streamed once per workgroup in tiles of 32 keys, software-pipelined:
-//   iteration j:  issue the buffer loads of tile j+1's packed codes,
-//                 compute tile j from LDS,
-//                 dequantize tile j+1 into the other LDS buffer,
+//   iteration j:  issue the buffer loads of tile j+2's packed codes,
+//                 S^T of tile j from LDS (MFMA),
+//                 dequantize tile j+1 (loaded one iteration earlier) into the
+//                 other LDS buffer while those MFMAs run,
+//                 softmax and O of tile j,
 //                 one barrier.
 //   Dequantization (shared by the workgroup's waves through LDS):
-//   - every thread owns fixed items (one key x 8 channels of K or of V) and
-//     keeps the binary16 (block, channel) statistics of its key's current
-//     block in registers, refreshed from LDS only when the key crosses into the
-//     next block;
+//   - the (block, channel) statistics of the whole prefix are staged in LDS;
+//     every thread owns fixed items (one key x 8 channels of K or of V) and
+//     keeps its key's current block's binary16 statistics in registers,
+//     refreshed only when the key crosses into the next block;
 //   - k_hat = fma(code, s, z) in fp32 straight from the binary16 statistics
 //     (v_fma_mix_f32; INT4 codes spread to bytes and converted with
 //     v_cvt_f32_ubyteN); k_hat is split into a truncated bf16 high part and a
@@ -51,7 +53,6 @@ constexpr int KPAD = 8;                 // K tile row padding (elements)
 constexpr int VROW = KT / 2 + 1;        // V^T row stride in dwords (odd)
 constexpr int kMaxWaves = 8;
 constexpr float kRescaleLog2 = 8.0f;    // lazy-rescale slack, log2 units
-constexpr int kStatsLdsHalves = 16384;  // 32 KB of binary16 statistics
 
 // byte n of a 32-bit word to fp32 (one instruction)
 template <int N>
@@ -117,12 +118,14 @@ __device__ __forceinline__ void codes_f32(uint32_t w, float c[8]) {
 // Raw buffer view of key tile j of one (b, h)'s packed prefix.  The hardware
 // range check covers the per-lane offset only (not the scalar offset), so the
 // tile's start goes into the base address and the record count is what is
-// left of the prefix: loads past the prefix's end return 0 and never leave it.
+// left of the prefix: loads past the prefix's end return 0 and never leave it;
+// a tile past the prefix gets zero records, so its loads touch no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* prefix, int prefix_bytes,
                                                             int tile_bytes, int j) {
   const int off = j * tile_bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(prefix + off), (short)0,
-                                           prefix_bytes - off, 0x00020000 /* 32-bit data format */);
+  const int left = prefix_bytes > off ? prefix_bytes - off : 0;  // past the prefix: none
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(prefix + off), (short)0, left,
+                                           0x00020000 /* 32-bit data format */);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,11 +222,9 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     const int64_t so = (((int64_t)b * p.H + h) * p.NB + f.block) * D + ch;
     f.zero[tensor][so] = gst.zb;
     f.scale[tensor][so] = gst.sb;
-    if (st_lds) {
-      _Float16* srow = st_lds + ((f.block * 2 + tensor) * 2) * D;
-      srow[ch] = __builtin_bit_cast(_Float16, gst.zb);
-      srow[D + ch] = __builtin_bit_cast(_Float16, gst.sb);
-    }
+    _Float16* srow = st_lds + ((f.block * 2 + tensor) * 2) * D;
+    srow[ch] = __builtin_bit_cast(_Float16, gst.zb);
+    srow[D + ch] = __builtin_bit_cast(_Float16, gst.sb);
     zi[(tensor * 2 + 0) * kWave + ch] = gst.zf;
     zi[(tensor * 2 + 1) * kWave + ch] = gst.inv;
   }
@@ -295,7 +296,6 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const bool q_ok = q < p.n;
   const bool wave_live = qt * NW * 32 + wave * 32 < p.n;
   const int nkb = p.n_kblocks;
-  const bool stats_lds = p.stats_in_lds != 0;
   const int64_t stat_base = (int64_t)bh * p.NB * D;
   const int n_prefix = p.n_prefix;
   const int n_tiles = (n_prefix + KT - 1) / KT;
@@ -304,7 +304,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   // dequantized; the statistics slot of block k in LDS is filled here, the
   // copy below skips it; the barrier after the copy publishes everything).
   if constexpr (FUSE != 0) {
-    quantize_block_wg<D, BITS, NW, FUSE == 2>(p, b, h, tid, stats_lds ? st : nullptr,
+    quantize_block_wg<D, BITS, NW, FUSE == 2>(p, b, h, tid, st,
                                               reinterpret_cast<float*>(&k_hi[0][0][0]));
   }
 
@@ -328,11 +328,14 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     s_shift[i] = (byte & 3) * 8;
   }
 
-  uint32_t pre[MAXI], pre2[MAXI];  // prefetched packed bits of the next tile
-  // fused launch: block k's rows are written below; tile 0 is fetched after
-  // that unless it ends before block k
+  // Packed bits in flight: tile j lands in register set A (j even) or B (j
+  // odd) two iterations before its dequantization, so the wait for one set
+  // leaves the newer set's loads outstanding.
+  uint32_t preA[MAXI], pre2A[MAXI], preB[MAXI], pre2B[MAXI];
+  // fused launch: block k's rows are written below; tile 0 is fetched before
+  // that only if it ends before block k, tile 1 always after
   const bool early0 = FUSE == 0 || (int)p.fz.off >= KT;
-  auto issue_loads = [&](int j) {
+  auto issue_loads = [&](int j, uint32_t (&pre)[MAXI], uint32_t (&pre2)[MAXI]) {
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpfx, pfx_bytes, tile_bytes, j);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpfx, pfx_bytes, tile_bytes, j);
 #pragma unroll
@@ -343,11 +346,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         pre2[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i] + 4, 0, 0);
     }
   };
-  if (early0) issue_loads(0);
+  if (early0) issue_loads(0, preA, pre2A);
 
   // ---- block ends and statistics to LDS, Q operand to registers -------------
   for (int i = tid; i < nkb; i += NT) blk_end[i] = p.block_end[i];
-  if (stats_lds) {  // 8 binary16 values per copy; a fused launch writes block k's
+  {  // 8 binary16 values per copy; a fused launch writes block k's
     const int nkb_copy = FUSE != 0 ? nkb - 1 : nkb;
     for (int i = tid; i < nkb_copy * 2 * CPR; i += NT) {
       const int blk = i / (2 * CPR);
@@ -373,19 +376,16 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     }
   }
   __syncthreads();  // blk_end, statistics and (fused) block k's rows visible
-  if (!early0) issue_loads(0);
+  if (!early0) issue_loads(0, preA, pre2A);
+  issue_loads(1, preB, pre2B);  // no records past the prefix: reads nothing
 
-  // binary16 statistics (8 channels of z and s) of one block for one tensor
+  // binary16 statistics (8 channels of z and s) of one block for one tensor,
+  // from LDS only (a read that may also go to global memory compiles to a flat
+  // load, whose wait would also drain the next tile's prefetch)
   auto load_stats = [&](int blk, int tensor, int cg, f16x8& z, f16x8& s) {
-    if (stats_lds) {
-      const _Float16* zr = st + ((blk * 2 + tensor) * 2) * D + 8 * cg;
-      z = *reinterpret_cast<const f16x8*>(zr);
-      s = *reinterpret_cast<const f16x8*>(zr + D);
-    } else {
-      const int64_t so = stat_base + (int64_t)blk * D + 8 * cg;
-      z = *reinterpret_cast<const f16x8*>((tensor == 0 ? p.kzero : p.vzero) + so);
-      s = *reinterpret_cast<const f16x8*>((tensor == 0 ? p.kscale : p.vscale) + so);
-    }
+    const _Float16* zr = st + ((blk * 2 + tensor) * 2) * D + 8 * cg;
+    z = *reinterpret_cast<const f16x8*>(zr);
+    s = *reinterpret_cast<const f16x8*>(zr + D);
   };
 
   // per-slot cache of the current block's statistics
@@ -398,7 +398,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     load_stats(0, s_tensor[i], s_cg[i], s_z[i], s_s[i]);
   }
 
-  auto dequant = [&](int j, int buf) {
+  auto dequant = [&](int j, int buf, const uint32_t (&pre)[MAXI], const uint32_t (&pre2)[MAXI]) {
     const int t0 = j * KT;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
@@ -470,14 +470,17 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   float l_run = 0.0f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  dequant(0, 0);
+  dequant(0, 0, preA, pre2A);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // tile j: cur holds tile j+1's packed bits (issued one iteration earlier),
+  // tile j+2's loads go into nxt
+  auto step = [&](int j, const uint32_t (&cur)[MAXI], const uint32_t (&cur2)[MAXI],
+                  uint32_t (&nxt)[MAXI], uint32_t (&nxt2)[MAXI]) {
     const int t0 = j * KT;
     const int buf = j & 1;
     const bool has_next = j + 1 < n_tiles;
-    if (has_next) issue_loads(j + 1);
+    issue_loads(j + 2, nxt, nxt2);  // unconditional: past the prefix it reads nothing
 
     if (wave_live) {
       // ---- S^T = K_hat Q^T -------------------------------------------------
@@ -502,6 +505,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      // the next tile's dequantization runs while these MFMAs complete
+      if (has_next) dequant(j + 1, buf ^ 1, cur, cur2);
 
       // ---- online softmax (log2 domain) -----------------------------------
       if (t0 + KT > n_prefix) {
@@ -554,9 +559,15 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       }
     }
 
-    if (has_next) dequant(j + 1, buf ^ 1);
+    if (!wave_live && has_next) dequant(j + 1, buf ^ 1, cur, cur2);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, preB, pre2B, preA, pre2A);
+    step(j + 1, preA, pre2A, preB, pre2B);
   }
+  if (j < n_tiles) step(j, preB, pre2B, preA, pre2A);
 
   // ---- normalize and store (fp32) ----------------------------------------
   const float l_tot = sum_xor32(l_run);
@@ -1024,7 +1035,6 @@ template <int D, int BITS, int QT, int FUSE = 0>
 hipError_t launch_small(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = 1;
-  a.stats_in_lds = 1;
   const int64_t grid = ((int64_t)p.B * p.H + kSmallWaves - 1) / kSmallWaves;
   hipLaunchKernelGGL((attend_small_kernel<D, BITS, QT, FUSE>), dim3((unsigned)grid),
                      dim3(kSmallWaves * kWave), 0, s, a);
@@ -1035,9 +1045,9 @@ template <int D, int BITS, int NW, int FUSE = 0>
 hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = (p.n + NW * 32 - 1) / (NW * 32);
-  const int stats_halves = p.n_kblocks * 4 * D;
-  a.stats_in_lds = stats_halves <= kStatsLdsHalves;
-  const size_t dyn = a.stats_in_lds ? (size_t)stats_halves * sizeof(_Float16) : 0;
+  // every block's statistics in LDS: at most 64 blocks x 4 x D binary16
+  // (32 KB at head_dim 64, 64 KB at 128)
+  const size_t dyn = (size_t)p.n_kblocks * 4 * D * sizeof(_Float16);
   const int64_t grid = (int64_t)p.B * p.H * a.q_tiles;
   hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE>), dim3((unsigned)grid), dim3(NW * kWave),
                      dyn, s, a);

@@ -195,7 +195,6 @@ struct AttendParams {
   int32_t n_kblocks;  // blocks attended: k + 1
   int32_t q_tiles;    // query tiles per (b, h)
   float scale_log2;   // softmax scale * log2(e)
-  int32_t stats_in_lds;  // prefix statistics staged in LDS as fp32
   int32_t block_end[KVQ_MAX_BLOCKS];
   FuseParams fz;  // used by the fused launch only
 };
