@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="quantize and attend with separate calls for every block")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="run this many of the workload's layers (0: all); for shapes whose "
+                         "inputs for every layer do not fit in HBM at once")
     return ap.parse_args()
 
 
@@ -188,6 +191,8 @@ def main():
     from visual_autoregressive_kv_amd import kvq as kb
 
     wl = vi.WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_(layers=min(args.layers, wl.layers))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = K.lib()
