@@ -141,10 +141,15 @@ struct QuantParams {
   int32_t rpt;         // rows per thread per pass
 };
 
+// The chunk-per-thread kernels (pack, unpack, dequantize) are launched in
+// pieces of at most kMaxLaunchWGs workgroups; chunk0 is a piece's first chunk.
+constexpr int64_t kMaxLaunchWGs = (int64_t)1 << 22;
+
 struct PackParams {
   const uint8_t* codes;
   uint8_t* dst;
   int64_t n_rows, dst_stride, n_chunks;
+  int64_t chunk0;
   int32_t row_len, bits, chunks_per_row, R;
   int32_t contiguous;  // dst rows back to back and row_len % 8 == 0
 };
@@ -153,6 +158,7 @@ struct UnpackParams {
   const uint8_t* src;
   uint8_t* codes;
   int64_t n_rows, src_stride, n_chunks;
+  int64_t chunk0;
   int32_t row_len, bits, chunks_per_row;
 };
 
@@ -162,6 +168,7 @@ struct DequantParams {
   const uint16_t* scale;
   float* out;
   int64_t T_cache, T_out, n_chunks;
+  int64_t chunk0;
   int32_t H, D, bits, R, NB;
   int32_t n_filled;
   int32_t block_end[KVQ_MAX_BLOCKS];  // exclusive prefix ends

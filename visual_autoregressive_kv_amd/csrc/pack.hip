@@ -27,7 +27,8 @@ __device__ __forceinline__ uint64_t pack8(uint64_t codes8, int bits, int count) 
 
 __global__ __launch_bounds__(kWG) void pack_kernel(PackParams p) {
   __shared__ __align__(16) uint8_t stage[kWG * 8 + 32];
-  const int64_t chunk = (int64_t)blockIdx.x * kWG + threadIdx.x;
+  const int64_t first = p.chunk0 + (int64_t)blockIdx.x * kWG;  // the workgroup's first chunk
+  const int64_t chunk = first + threadIdx.x;
   const bool ok = chunk < p.n_chunks;
   const int64_t row = ok ? chunk / p.chunks_per_row : 0;
   const int c = ok ? (int)(chunk - row * p.chunks_per_row) : 0;
@@ -46,7 +47,6 @@ __global__ __launch_bounds__(kWG) void pack_kernel(PackParams p) {
   const int nb = ok ? (p.bits * count + 7) / 8 : 0;
   if (p.contiguous) {
     // the workgroup's chunks map to one contiguous span of dst
-    const int64_t first = (int64_t)blockIdx.x * kWG;
     const int64_t last = min(first + kWG, p.n_chunks);
     uint8_t* dst = p.dst + first * p.bits;
     const int nbytes = (int)((last - first) * p.bits);
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kWG) void pack_kernel(PackParams p) {
 }
 
 __global__ __launch_bounds__(kWG) void unpack_kernel(UnpackParams p) {
-  const int64_t chunk = (int64_t)blockIdx.x * kWG + threadIdx.x;
+  const int64_t chunk = p.chunk0 + (int64_t)blockIdx.x * kWG + threadIdx.x;
   if (chunk >= p.n_chunks) return;
   const int64_t row = chunk / p.chunks_per_row;
   const int c = (int)(chunk - row * p.chunks_per_row);
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kWG) void unpack_kernel(UnpackParams p) {
 
 // one thread = 8 channels of one cached token
 __global__ __launch_bounds__(kWG) void dequant_kernel(DequantParams p) {
-  const int64_t chunk = (int64_t)blockIdx.x * kWG + threadIdx.x;
+  const int64_t chunk = p.chunk0 + (int64_t)blockIdx.x * kWG + threadIdx.x;
   if (chunk >= p.n_chunks) return;
   const int cpr = p.D / 8;
   const int64_t rowid = chunk / cpr;  // (b*H + h) * T_out + t
@@ -159,25 +159,30 @@ __global__ __launch_bounds__(256) void unpack_words_kernel(const uint32_t* __res
   }
 }
 
-hipError_t launch_pack(const PackParams& p, hipStream_t s) {
-  if (p.n_chunks == 0) return hipSuccess;
-  const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
-  return hipGetLastError();
+// one launch per piece of at most kMaxLaunchWGs workgroups, so a grid never
+// exceeds the 32-bit work-item count of a dispatch
+template <typename Params>
+hipError_t launch_pieces(void (*kernel)(Params), const Params& p, hipStream_t s) {
+  const int64_t wgs = (p.n_chunks + kWG - 1) / kWG;
+  for (int64_t w0 = 0; w0 < wgs; w0 += kMaxLaunchWGs) {
+    Params a = p;
+    a.chunk0 = w0 * kWG;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)std::min(kMaxLaunchWGs, wgs - w0)), dim3(kWG), 0, s,
+                       a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
+hipError_t launch_pack(const PackParams& p, hipStream_t s) { return launch_pieces(pack_kernel, p, s); }
+
 hipError_t launch_unpack(const UnpackParams& p, hipStream_t s) {
-  if (p.n_chunks == 0) return hipSuccess;
-  const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
-  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
-  return hipGetLastError();
+  return launch_pieces(unpack_kernel, p, s);
 }
 
 hipError_t launch_dequantize(const DequantParams& p, hipStream_t s) {
-  if (p.n_chunks == 0) return hipSuccess;
-  const int64_t grid = (p.n_chunks + kWG - 1) / kWG;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, p);
-  return hipGetLastError();
+  return launch_pieces(dequant_kernel, p, s);
 }
 
 hipError_t launch_pack_words(const uint8_t* codes, uint8_t* dst, int64_t n, int bits,
