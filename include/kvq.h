@@ -90,6 +90,9 @@ extern "C" {
  *               KVQ_E_UNSUPPORTED for it.
  *   block_tokens[k]  tokens of block k (>= 1), e.g. s*s for next-scale
  *                    prediction at scale s, or a frame's tokens for video
+ * The decode calls (kvq_quantize_block, kvq_attend_packed, kvq_quantize_attend)
+ * take batch * heads < 2^25 (else KVQ_E_UNSUPPORTED), so that each of their
+ * launches stays under 2^32 work-items.
  */
 typedef struct {
   int32_t batch, heads, head_dim, bits, n_blocks, pack_mode;
@@ -135,7 +138,8 @@ int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
  *                 inputs are not screened and a non-finite or out-of-range
  *                 input leaves that group's outputs undefined.
  * Errors: KVQ_E_INVAL (layout, block, dtype, NULL or misaligned pointer),
- * KVQ_E_UNSUPPORTED (bits or head_dim not built), KVQ_E_DEVICE.
+ * KVQ_E_UNSUPPORTED (bits or head_dim not built, pack_mode 1, batch * heads >=
+ * 2^25), KVQ_E_DEVICE.
  */
 int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtype,
                        const void* k_src, const void* v_src, kvq_cache k_cache,

@@ -73,6 +73,15 @@ def test_quantize_argument_errors_return_before_launch():
     L32 = K.make_layout(2, 3, 32, 4, (1, 4, 9))
     assert q(C.byref(L32), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == \
         kb.E_UNSUPPORTED
+    # 2^25 (sequence, head) pairs: valid for the byte accounting, too many for one decode call
+    Lbig = K.make_layout(1 << 15, 1 << 10, 64, 4, (1, 4, 9))
+    assert K.kvq_bytes(Lbig, 3)[0] == (1 << 25) * 14 * 32
+    assert q(C.byref(Lbig), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None, None) == \
+        kb.E_UNSUPPORTED
+    assert lib.kvq_attend_packed(C.byref(Lbig), 0, FAKE, _cache(), _cache(), 0.0, FAKE, None) == \
+        kb.E_UNSUPPORTED
+    assert lib.kvq_quantize_attend(C.byref(Lbig), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(),
+                                   _cache(), 0.0, FAKE, None, None) == kb.E_UNSUPPORTED
 
 
 def test_attend_and_pack_argument_errors_return_before_launch():

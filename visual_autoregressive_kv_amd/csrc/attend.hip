@@ -1036,6 +1036,7 @@ hipError_t launch_small(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = 1;
   const int64_t grid = ((int64_t)p.B * p.H + kSmallWaves - 1) / kSmallWaves;
+  if (!dispatch_fits(grid, kSmallWaves * kWave)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attend_small_kernel<D, BITS, QT, FUSE>), dim3((unsigned)grid),
                      dim3(kSmallWaves * kWave), 0, s, a);
   return hipGetLastError();
@@ -1049,6 +1050,7 @@ hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   // (32 KB at head_dim 64, 64 KB at 128)
   const size_t dyn = (size_t)p.n_kblocks * 4 * D * sizeof(_Float16);
   const int64_t grid = (int64_t)p.B * p.H * a.q_tiles;
+  if (!dispatch_fits(grid, NW * kWave)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE>), dim3((unsigned)grid), dim3(NW * kWave),
                      dyn, s, a);
   return hipGetLastError();

@@ -47,6 +47,15 @@ int gpu_supported(const kvq_layout* L) {
   return KVQ_OK;
 }
 
+// Sequences x heads per decode call.  Below this bound every quantize and
+// attention launch of a call that fits in HBM stays under 2^32 work-items per
+// dispatch (the widest per pair, the small-block attention, takes 64).
+constexpr int64_t kMaxDecodePairs = (int64_t)1 << 25;
+
+int decode_pairs_ok(const kvq_layout* L) {
+  return (int64_t)L->batch * L->heads < kMaxDecodePairs ? KVQ_OK : KVQ_E_UNSUPPORTED;
+}
+
 int64_t offset_of(const kvq_layout* L, int32_t block) {
   int64_t off = 0;
   for (int i = 0; i < block; ++i) off += L->block_tokens[i];
@@ -92,7 +101,8 @@ int make_quant_params(const kvq_layout* layout, int32_t block, int32_t src_dtype
   if (!k_src || !v_src || !aligned16(k_src) || !aligned16(v_src)) return KVQ_E_INVAL;
   if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
   if (status_dev && (reinterpret_cast<uintptr_t>(status_dev) & 3)) return KVQ_E_INVAL;
-  const int sup = gpu_supported(layout);
+  int sup = gpu_supported(layout);
+  if (sup == KVQ_OK) sup = decode_pairs_ok(layout);
   if (sup != KVQ_OK) return sup;
   QuantParams& p = *out;
   memset(&p, 0, sizeof(p));
@@ -127,7 +137,8 @@ int make_attend_params(const kvq_layout* layout, int32_t block, const uint16_t* 
   if (!q_bf16 || !out || !aligned16(q_bf16) || !aligned16(out)) return KVQ_E_INVAL;
   if (!cache_ok(k_cache) || !cache_ok(v_cache)) return KVQ_E_INVAL;
   if (!(scale == scale) || isinf(scale)) return KVQ_E_INVAL;
-  const int sup = gpu_supported(layout);
+  int sup = gpu_supported(layout);
+  if (sup == KVQ_OK) sup = decode_pairs_ok(layout);
   if (sup != KVQ_OK) return sup;
   AttendParams& p = *dst;
   memset(&p, 0, sizeof(p));

@@ -141,6 +141,11 @@ struct QuantParams {
   int32_t rpt;         // rows per thread per pass
 };
 
+// a dispatch holds at most 2^32 - 1 work-items
+inline bool dispatch_fits(int64_t groups, int threads) {
+  return groups * threads <= (int64_t)UINT32_MAX;
+}
+
 // The chunk-per-thread kernels (pack, unpack, dequantize) are launched in
 // pieces of at most kMaxLaunchWGs workgroups; chunk0 is a piece's first chunk.
 constexpr int64_t kMaxLaunchWGs = (int64_t)1 << 22;

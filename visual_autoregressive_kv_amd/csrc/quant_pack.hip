@@ -455,6 +455,7 @@ hipError_t launch_sliced(const QuantParams& p, hipStream_t s) {
   const int n_slices = (p.n + kSliceRows<D> - 1) / kSliceRows<D>;
   // parked extremes must fit the block's rows
   if ((int64_t)n_slices * 8 * D > (int64_t)p.n * p.R) return hipErrorInvalidValue;
+  if (!dispatch_fits(p.n_tiles * n_slices, kWG)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(p.n_tiles * n_slices));
   hipLaunchKernelGGL((slice_extremes_kernel<D, F32, CHECK>), grid, dim3(kWG), 0, s, p, n_slices);
   hipLaunchKernelGGL((slice_stats_kernel<D, BITS, F32, CHECK>), dim3((unsigned)p.n_tiles), dim3(D), 0,
@@ -471,6 +472,7 @@ hipError_t launch_t(const QuantParams& p, hipStream_t s) {
   const bool check = p.status != nullptr;
   if (stream && p.n_tiles < kSliceTiles)
     return check ? launch_sliced<D, BITS, F32, true>(p, s) : launch_sliced<D, BITS, F32, false>(p, s);
+  if (!dispatch_fits(grid, kWG)) return hipErrorInvalidConfiguration;
   dim3 g((unsigned)grid), blk(kWG);
   if (check) {
     if (stream)
