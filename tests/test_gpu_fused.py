@@ -43,7 +43,11 @@ def decode_both_ways(oracle, wl, layer=0, scale=0.0):
     vi.WORKLOADS["var_d24_b128_int4"].with_(batch=2, layers=1),
     vi.Workload("edge", 1, 1, 3, 64, 3, (1, 7, 32, 33, 2), "bf16", rope=True, seed=13),
     vi.Workload("edge128", 1, 2, 3, 128, 4, (5, 31, 40), "bf16", seed=17),
-], ids=["tiny_f32", "d20_int4", "d20_int3_rope", "d24_int4", "edge_int3", "edge_d128"])
+    # 23 blocks: the one-wave fused kernel while the statistics fit its LDS (8
+    # blocks), then two launches for short blocks, the workgroup kernel for 40
+    vi.Workload("many_blocks", 1, 2, 3, 64, 3, (1,) * 20 + (5, 40, 3), "bf16", seed=29),
+], ids=["tiny_f32", "d20_int4", "d20_int3_rope", "d24_int4", "edge_int3", "edge_d128",
+        "many_blocks"])
 def test_fused_matches_two_calls_and_oracle(oracle, wl):
     kf, vf, ks, vs, ko, vo, steps = decode_both_ways(oracle, wl)
     assert_cache_equal(kf, ko, "fused K")
