@@ -6,8 +6,10 @@ One step is one full block-by-block decode pass of the workload: for every
 scale k of the 10-scale VAR schedule and every layer, quantize + bit-pack the
 freshly decoded block's K and V into that layer's packed cache, then run
 block-causal attention of the block's queries over the packed cache, both in
-one launch (kvq_quantize_attend; head_dim 64, blocks of up to 256 tokens);
---unfused calls kvq_quantize_block then kvq_attend_packed for every block.
+one launch (kvq_quantize_attend; head_dim 64, blocks of up to 256 tokens).
+Other blocks, and every block with --unfused, call kvq_quantize_block then
+kvq_attend_packed_split (up to 8 key ranges per query tile in a workspace
+allocated up front; --no-split calls kvq_attend_packed instead).
 Inputs (K, V, Q of every block of every layer, bf16, synthetic VAR-shaped
 data drawn on the device) and caches are
 resident in HBM before the timed region; every layer has its own buffers, so
@@ -42,6 +44,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "var_d20_b128_int4"
 FUSED_MAX_TOKENS = 256  # blocks kvq_quantize_attend runs as one launch (head_dim 64, bf16)
+MAX_SPLITS = 8  # key ranges per query tile for kvq_attend_packed_split
 KERNEL_SOURCES = {
     "quant_pack": "visual_autoregressive_kv_amd/csrc/quant_pack.hip",
     "attend": "visual_autoregressive_kv_amd/csrc/attend.hip",
@@ -60,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="quantize and attend with separate calls for every block")
+    ap.add_argument("--no-split", action="store_true",
+                    help="attend with kvq_attend_packed instead of kvq_attend_packed_split")
     ap.add_argument("--layers", type=int, default=0,
                     help="run this many of the workload's layers (0: all); for shapes whose "
                          "inputs for every layer do not fit in HBM at once")
@@ -244,6 +249,13 @@ def main():
         return (not args.unfused and wl.head_dim == 64 and wl.blocks[j] <= FUSED_MAX_TOKENS
                 and (wl.src == "bf16" or wl.blocks[j] <= 32))
 
+    # workspace of kvq_attend_packed_split, sized for the largest unfused block
+    split = not args.no_split
+    ws_bytes = max([K.kvq_attend_split_workspace(L, j, MAX_SPLITS) for j in range(NB)
+                    if not fused(j)] or [0]) if split else 0
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_n = ws.data_ptr(), C.c_uint64(ws.numel())
+
     calls = []  # (kind, block, function, arguments), in launch order
     for j in range(NB):
         for l in range(wl.layers):
@@ -258,9 +270,14 @@ def main():
                 calls.append(("quant_pack", j, lib.kvq_quantize_block,
                               (Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
                                kC[l], vC[l], None, sh)))
-                calls.append(("attend", j, lib.kvq_attend_packed,
-                              (Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
-                               Out[l][j].data_ptr(), sh)))
+                if split:
+                    calls.append(("attend", j, lib.kvq_attend_packed_split,
+                                  (Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
+                                   Out[l][j].data_ptr(), MAX_SPLITS, ws_ptr, ws_n, sh)))
+                else:
+                    calls.append(("attend", j, lib.kvq_attend_packed,
+                                  (Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
+                                   Out[l][j].data_ptr(), sh)))
     # one checked call of each kind through the binding before the raw loop
     K.kvq_quantize_block(L, 0, Kin[0][0], Vin[0][0], kcs[0], vcs[0])
     K.kvq_attend_packed(L, 0, Qin[0][0], kcs[0], vcs[0], Out[0][0])
@@ -383,6 +400,9 @@ def main():
         "per_block_us": per_block_us,
         "roofline": roofline,
     }
+    if "attend" in kinds:
+        out["config"]["attention_call"] = ("kvq_attend_packed" if not split else
+                                           f"kvq_attend_packed_split (max {MAX_SPLITS} key ranges)")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

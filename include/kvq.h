@@ -181,6 +181,38 @@ int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q
                       float* out, hipStream_t stream);
 
 /*
+ * kvq_attend_packed_split -- kvq_attend_packed for long prefixes and few query
+ * tiles (next-frame video: 40 heads x 1560 queries over up to 16 frames of
+ * 1560 keys), where one workgroup per (sequence, head, 256 queries) leaves
+ * most of the GPU idle in the grid's last round.  The key prefix of every
+ * query tile is cut into up to max_splits ranges of whole 32-key tiles; each
+ * range is attended by its own workgroup into a partial result (unnormalized
+ * output, running maximum, softmax denominator) in `workspace`, and a second
+ * launch merges the partials by log-sum-exp.  Same arithmetic per key as
+ * kvq_attend_packed, summed in another order: results agree with it and the
+ * exact attention within the same 2e-3 bound.
+ *   max_splits  1..64, an upper bound: blocks of at most 128 queries, short
+ *               prefixes (fewer than 16 key tiles per range) and grids that
+ *               already hold about eight workgroups per CU use fewer ranges,
+ *               down to one (then this is exactly kvq_attend_packed)
+ *   workspace   caller-owned device memory of at least workspace_bytes >=
+ *               kvq_attend_split_workspace(layout, block, max_splits) bytes,
+ *               16-byte aligned, not overlapping any other argument; its
+ *               contents on entry are ignored and on return unspecified
+ * Errors as kvq_attend_packed; KVQ_E_INVAL also for max_splits out of range
+ * or a missing, misaligned or too small workspace.
+ */
+int kvq_attend_packed_split(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
+                            kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
+                            float* out, int32_t max_splits, void* workspace,
+                            uint64_t workspace_bytes, hipStream_t stream);
+
+/* workspace bytes kvq_attend_packed_split needs for block `block` and
+ * max_splits ranges: max_splits * B * n_k * H * (D + 2) * 4.  Host only. */
+int kvq_attend_split_workspace(const kvq_layout* layout, int32_t block, int32_t max_splits,
+                               uint64_t* bytes);
+
+/*
  * kvq_quantize_attend -- the decode step of one layer for block k (VAR-Q
  * abstract: the block is quantized when the generation loop hands it over,
  * then the block's queries attend to the packed cache of blocks 0..k).

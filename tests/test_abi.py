@@ -109,6 +109,32 @@ def test_attend_and_pack_argument_errors_return_before_launch():
     assert lib.kvq_stream_copy(FAKE, FAKE, 0, None) == kb.OK
 
 
+def test_attend_split_argument_errors_return_before_launch():
+    lib = K.lib()
+    L = K.make_layout(1, 40, 128, 3, (1560, 1560))
+    E = kb.E_INVAL
+    need = C.c_uint64()
+    assert lib.kvq_attend_split_workspace(C.byref(L), 1, 8, C.byref(need)) == kb.OK
+    assert need.value == 8 * 1560 * 40 * (128 + 2) * 4
+    assert lib.kvq_attend_split_workspace(C.byref(L), 2, 8, C.byref(need)) == E  # block
+    assert lib.kvq_attend_split_workspace(C.byref(L), 1, 0, C.byref(need)) == E
+    assert lib.kvq_attend_split_workspace(C.byref(L), 1, 65, C.byref(need)) == E
+    assert lib.kvq_attend_split_workspace(C.byref(L), 1, 8, None) == E
+    n = need.value
+    f = lib.kvq_attend_packed_split
+
+    def call(block=1, ms=8, ws=FAKE, nb=n, layout=L):
+        return f(C.byref(layout), block, FAKE, _cache(), _cache(), 0.0, FAKE, ms, ws, nb, None)
+
+    assert call(block=2) == E
+    assert call(ms=0) == E
+    assert call(ms=65) == E
+    assert call(ws=None) == E
+    assert call(ws=FAKE + 8) == E       # workspace alignment
+    assert call(nb=n - 1) == E          # workspace too small
+    assert call(layout=K.make_layout(1, 40, 128, 5, (1560, 1560))) == kb.E_UNSUPPORTED
+
+
 def test_layout_limits():
     lib = K.lib()
     L = K.make_layout(2, 3, 64, 4, (1,) * 64)

@@ -8,7 +8,7 @@ streams only).
 """
 from .kvq import (  # noqa: F401
     BF16, F32, KvqError, Layout, S_NONFINITE, S_RANGE, alloc_cache, cache_shapes,
-    header_symbols, kvq_attend_packed, kvq_bytes, kvq_dequantize, kvq_pack,
-    kvq_quantize_attend, kvq_quantize_block, kvq_stream_copy, kvq_unpack, kvq_version, lib,
-    make_layout,
+    header_symbols, kvq_attend_packed, kvq_attend_packed_split, kvq_attend_split_workspace,
+    kvq_bytes, kvq_dequantize, kvq_pack, kvq_quantize_attend, kvq_quantize_block,
+    kvq_stream_copy, kvq_unpack, kvq_version, lib, make_layout,
 )

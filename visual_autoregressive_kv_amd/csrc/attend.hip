@@ -264,7 +264,10 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
 
 // FUSE: 0 attention only; 1/2 quantize block k from bf16 first (2: with input
 // checks); the launcher uses it with one query tile per (sequence, head).
-template <int D, int BITS, int NW, int FUSE>
+// SPLIT: the workgroup attends only key-tile range sp of p.splits (whole
+// tiles, balanced) and writes its unnormalized output, running maximum and
+// denominator to the workspace for attend_merge_kernel (attention only).
+template <int D, int BITS, int NW, int FUSE, int SPLIT = 0>
 // Register caps chosen for residency: 2-wave workgroups at 3 waves per SIMD and
 // 4-wave workgroups at 4 (a few dwords spill; measured faster on VAR-d20 than
 // the extra dispatch rounds without the cap).
@@ -288,8 +291,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const int lane = tid % kWave;
   const int g = lane >> 5;    // lane group: which 8 of each 16 contraction slots
   const int col = lane & 31;  // this lane's query (S^T / O^T column)
-  const int bh = blockIdx.x / p.q_tiles;
-  const int qt = blockIdx.x - bh * p.q_tiles;
+  static_assert(SPLIT == 0 || FUSE == 0, "key ranges are for the attention-only launch");
+  const int wg = SPLIT ? (int)(blockIdx.x / p.splits) : (int)blockIdx.x;
+  const int sp = SPLIT ? (int)blockIdx.x - wg * p.splits : 0;
+  const int bh = wg / p.q_tiles;
+  const int qt = wg - bh * p.q_tiles;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int q = qt * NW * 32 + wave * 32 + col;
@@ -299,6 +305,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const int64_t stat_base = (int64_t)bh * p.NB * D;
   const int n_prefix = p.n_prefix;
   const int n_tiles = (n_prefix + KT - 1) / KT;
+  // this workgroup's key tiles [j_begin, j_end): all, or one balanced range
+  const int j_begin = SPLIT ? (int)((int64_t)sp * n_tiles / p.splits) : 0;
+  const int j_end = SPLIT ? (int)((int64_t)(sp + 1) * n_tiles / p.splits) : n_tiles;
 
   // Fused launch: quantize block k first (k_hi is free until tile 0 is
   // dequantized; the statistics slot of block k in LDS is filled here, the
@@ -346,7 +355,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         pre2[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i] + 4, 0, 0);
     }
   };
-  if (early0) issue_loads(0, preA, pre2A);
+  if (early0) issue_loads(j_begin, preA, pre2A);
 
   // ---- block ends and statistics to LDS, Q operand to registers -------------
   for (int i = tid; i < nkb; i += NT) blk_end[i] = p.block_end[i];
@@ -376,8 +385,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     }
   }
   __syncthreads();  // blk_end, statistics and (fused) block k's rows visible
-  if (!early0) issue_loads(0, preA, pre2A);
-  issue_loads(1, preB, pre2B);  // no records past the prefix: reads nothing
+  if (!early0) issue_loads(j_begin, preA, pre2A);
+  issue_loads(j_begin + 1, preB, pre2B);  // no records past the prefix: reads nothing
 
   // binary16 statistics (8 channels of z and s) of one block for one tensor,
   // from LDS only (a read that may also go to global memory compiles to a flat
@@ -470,7 +479,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   float l_run = 0.0f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  dequant(0, 0, preA, pre2A);
+  dequant(j_begin, 0, preA, pre2A);
   __syncthreads();
 
   // tile j: cur holds tile j+1's packed bits (issued one iteration earlier),
@@ -478,8 +487,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   auto step = [&](int j, const uint32_t (&cur)[MAXI], const uint32_t (&cur2)[MAXI],
                   uint32_t (&nxt)[MAXI], uint32_t (&nxt2)[MAXI]) {
     const int t0 = j * KT;
-    const int buf = j & 1;
-    const bool has_next = j + 1 < n_tiles;
+    const int buf = (j - j_begin) & 1;
+    const bool has_next = j + 1 < j_end;
     issue_loads(j + 2, nxt, nxt2);  // unconditional: past the prefix it reads nothing
 
     if (wave_live) {
@@ -562,15 +571,36 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     if (!wave_live && has_next) dequant(j + 1, buf ^ 1, cur, cur2);
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 1 < n_tiles; j += 2) {
+  int j = j_begin;
+  for (; j + 1 < j_end; j += 2) {
     step(j, preB, pre2B, preA, pre2A);
     step(j + 1, preA, pre2A, preB, pre2B);
   }
-  if (j < n_tiles) step(j, preB, pre2B, preA, pre2A);
+  if (j < j_end) step(j, preB, pre2B, preA, pre2A);
+
+  const float l_tot = sum_xor32(l_run);
+  if constexpr (SPLIT) {
+    // ---- partial result of this key range: O unnormalized, m c, l ----------
+    if (q_ok) {
+      const int64_t row = ((int64_t)b * p.n + q) * p.H + h;
+      float* orow = p.ws_o + ((int64_t)sp * p.ws_rows + row) * D;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * r4 + 4 * g) =
+              f32x4{o[i][4 * r4 + 0], o[i][4 * r4 + 1], o[i][4 * r4 + 2], o[i][4 * r4 + 3]};
+      }
+      if (g == 0) {
+        float* ml = p.ws_ml + ((int64_t)sp * p.ws_rows + row) * 2;
+        ml[0] = m_run * c;  // log2 units: p = exp2(s c - ml[0])
+        ml[1] = l_tot;
+      }
+    }
+    return;
+  }
 
   // ---- normalize and store (fp32) ----------------------------------------
-  const float l_tot = sum_xor32(l_run);
   const float inv_l = 1.0f / l_tot;
   if (q_ok) {
     float* orow = p.out + (((int64_t)b * p.n + q) * p.H + h) * D;
@@ -1042,17 +1072,17 @@ hipError_t launch_small(const AttendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int BITS, int NW, int FUSE = 0>
+template <int D, int BITS, int NW, int FUSE = 0, int SPLIT = 0>
 hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = (p.n + NW * 32 - 1) / (NW * 32);
   // every block's statistics in LDS: at most 64 blocks x 4 x D binary16
   // (32 KB at head_dim 64, 64 KB at 128)
   const size_t dyn = (size_t)p.n_kblocks * 4 * D * sizeof(_Float16);
-  const int64_t grid = (int64_t)p.B * p.H * a.q_tiles;
+  const int64_t grid = (int64_t)p.B * p.H * a.q_tiles * (SPLIT ? p.splits : 1);
   if (!dispatch_fits(grid, NW * kWave)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE>), dim3((unsigned)grid), dim3(NW * kWave),
-                     dyn, s, a);
+  hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE, SPLIT>), dim3((unsigned)grid),
+                     dim3(NW * kWave), dyn, s, a);
   return hipGetLastError();
 }
 
@@ -1074,6 +1104,51 @@ hipError_t launch_t(const AttendParams& p, hipStream_t s) {
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
   if (head_dim == 64) return bits == 4 ? launch_t<64, 4>(p, s) : launch_t<64, 3>(p, s);
   return bits == 4 ? launch_t<128, 4>(p, s) : launch_t<128, 3>(p, s);
+}
+
+namespace {
+// Merge of the key-range partials written by attend_kernel<.., SPLIT = 1>:
+// with M = max_s ml_s (log2 units), out = sum_s 2^(ml_s - M) O_s divided by
+// sum_s 2^(ml_s - M) l_s, the log-sum-exp combination of softmax pieces.  One
+// thread per 4 channels of one output row (sequence, query, head).
+template <int D>
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttendParams p) {
+  constexpr int C4 = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / C4;
+  if (row >= p.ws_rows) return;
+  const int c4 = (int)(t - row * C4);
+  float m = -__builtin_inff();
+  for (int sp = 0; sp < p.splits; ++sp) m = fmaxf(m, p.ws_ml[((int64_t)sp * p.ws_rows + row) * 2]);
+  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  for (int sp = 0; sp < p.splits; ++sp) {
+    const int64_t r = (int64_t)sp * p.ws_rows + row;
+    const float w = __builtin_amdgcn_exp2f(p.ws_ml[r * 2] - m);
+    den = __builtin_fmaf(w, p.ws_ml[r * 2 + 1], den);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.ws_o + r * D + 4 * c4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) num[k] = __builtin_fmaf(w, o[k], num[k]);
+  }
+  const float inv = 1.0f / den;
+  *reinterpret_cast<f32x4*>(p.out + row * D + 4 * c4) =
+      f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+}
+
+template <int D, int BITS>
+hipError_t launch_split_t(const AttendParams& p, hipStream_t s) {
+  const int64_t merge_grid = (p.ws_rows * (D / 4) + 255) / 256;
+  if (!dispatch_fits(merge_grid, 256)) return hipErrorInvalidConfiguration;
+  const hipError_t e = launch_nw<D, BITS, kMaxWaves, 0, 1>(p, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)merge_grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attend_split(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
+  if (head_dim == 64) return bits == 4 ? launch_split_t<64, 4>(p, s) : launch_split_t<64, 3>(p, s);
+  return bits == 4 ? launch_split_t<128, 4>(p, s) : launch_split_t<128, 3>(p, s);
 }
 
 namespace {

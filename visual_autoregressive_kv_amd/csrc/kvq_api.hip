@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kvq_internal.h"
 
 namespace {
@@ -168,6 +170,30 @@ int make_attend_params(const kvq_layout* layout, int32_t block, const uint16_t* 
   return KVQ_OK;
 }
 
+// Key ranges per query tile of kvq_attend_packed_split: enough workgroups for
+// about eight per CU of the 256 on a gfx950 device, at least 16 key tiles (512
+// keys) per range, at most max_splits.  Blocks of at most 128 queries run the
+// kernels without ranges.
+constexpr int32_t kMaxSplits = 64;
+constexpr int64_t kSplitTargetWGs = 8 * 256;
+constexpr int64_t kMinSplitTiles = 16;
+
+int32_t pick_splits(const AttendParams& p, int32_t max_splits) {
+  if (p.n <= 128) return 1;
+  const int64_t wgs = (int64_t)p.B * p.H * ((p.n + 255) / 256);
+  const int64_t tiles = ((int64_t)p.n_prefix + 31) / 32;
+  int64_t sp = (kSplitTargetWGs + wgs - 1) / wgs;
+  sp = std::min<int64_t>(sp, tiles / kMinSplitTiles);
+  sp = std::min<int64_t>(sp, max_splits);
+  return (int32_t)std::max<int64_t>(sp, 1);
+}
+
+// partial outputs (head_dim floats) plus (max, denominator) per range and row
+uint64_t split_workspace_bytes(const kvq_layout* L, int32_t block, int32_t splits) {
+  const uint64_t rows = (uint64_t)L->batch * (uint64_t)L->block_tokens[block] * (uint64_t)L->heads;
+  return (uint64_t)splits * rows * ((uint64_t)L->head_dim + 2u) * 4u;
+}
+
 kvq_cache_const const_view(kvq_cache c) {
   kvq_cache_const r;
   r.codes = c.codes;
@@ -307,6 +333,34 @@ int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q
   const int rc = make_attend_params(layout, block, q_bf16, k_cache, v_cache, scale, out, &p);
   if (rc != KVQ_OK) return rc;
   return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+}
+
+int kvq_attend_split_workspace(const kvq_layout* layout, int32_t block, int32_t max_splits,
+                               uint64_t* bytes) {
+  if (validate_layout(layout) != KVQ_OK) return KVQ_E_INVAL;
+  if (block < 0 || block >= layout->n_blocks || !bytes) return KVQ_E_INVAL;
+  if (max_splits < 1 || max_splits > kMaxSplits) return KVQ_E_INVAL;
+  *bytes = split_workspace_bytes(layout, block, max_splits);
+  return KVQ_OK;
+}
+
+int kvq_attend_packed_split(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
+                            kvq_cache_const k_cache, kvq_cache_const v_cache, float scale,
+                            float* out, int32_t max_splits, void* workspace,
+                            uint64_t workspace_bytes, hipStream_t stream) {
+  AttendParams p;
+  const int rc = make_attend_params(layout, block, q_bf16, k_cache, v_cache, scale, out, &p);
+  if (rc != KVQ_OK) return rc;
+  if (max_splits < 1 || max_splits > kMaxSplits) return KVQ_E_INVAL;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < split_workspace_bytes(layout, block, max_splits))
+    return KVQ_E_INVAL;
+  p.splits = pick_splits(p, max_splits);
+  if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+  p.ws_rows = (int64_t)p.B * p.n * p.H;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + (int64_t)p.splits * p.ws_rows * layout->head_dim;
+  return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream));
 }
 
 int kvq_quantize_attend(const kvq_layout* layout, int32_t block, int32_t src_dtype,

@@ -209,6 +209,12 @@ struct AttendParams {
   float scale_log2;   // softmax scale * log2(e)
   int32_t block_end[KVQ_MAX_BLOCKS];
   FuseParams fz;  // used by the fused launch only
+  // key-range launch only: ranges per query tile and the partials'
+  // workspace, ws_o [splits][rows][D] and ws_ml [splits][rows][2] (rows = B n H)
+  int32_t splits;
+  int64_t ws_rows;
+  float* ws_o;
+  float* ws_ml;
 };
 
 hipError_t launch_quantize(const QuantParams& p, int head_dim, int bits, bool f32src,
@@ -222,6 +228,9 @@ hipError_t launch_unpack_words(const uint8_t* src, uint8_t* codes, int64_t n, in
                                hipStream_t s);
 hipError_t launch_dequantize(const DequantParams& p, hipStream_t s);
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s);
+// attention of blocks of more than 128 queries with the key prefix cut into
+// p.splits ranges (p.splits >= 2), then the merge of the partials
+hipError_t launch_attend_split(const AttendParams& p, int head_dim, int bits, hipStream_t s);
 // quantize block k (q) then attend its queries (a): one launch where a fused
 // kernel covers the shape, else the two launches in order
 hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,

@@ -88,6 +88,11 @@ def lib() -> C.CDLL:
         L.kvq_quantize_attend.restype = C.c_int
         L.kvq_quantize_attend.argtypes = [C.POINTER(Layout), i32, i32, vp, vp, vp, Cache, Cache,
                                           C.c_float, vp, vp, vp]
+        L.kvq_attend_packed_split.restype = C.c_int
+        L.kvq_attend_packed_split.argtypes = [C.POINTER(Layout), i32, vp, Cache, Cache, C.c_float,
+                                              vp, i32, vp, u64, vp]
+        L.kvq_attend_split_workspace.restype = C.c_int
+        L.kvq_attend_split_workspace.argtypes = [C.POINTER(Layout), i32, i32, C.POINTER(u64)]
         L.kvq_stream_copy.restype = C.c_int
         L.kvq_stream_copy.argtypes = [vp, vp, u64, vp]
         _lib = L
@@ -252,6 +257,29 @@ def kvq_attend_packed(layout: Layout, block: int, q: torch.Tensor, k_cache, v_ca
                                    _cache(layout, k_cache, "k_cache"),
                                    _cache(layout, v_cache, "v_cache"), float(scale),
                                    _dev(out, "out", torch.float32, shp), _stream(stream)))
+
+
+def kvq_attend_split_workspace(layout: Layout, block: int, max_splits: int) -> int:
+    """Workspace bytes of kvq_attend_packed_split for this block and max_splits."""
+    nbytes = C.c_uint64()
+    _check("kvq_attend_split_workspace",
+           lib().kvq_attend_split_workspace(C.byref(layout), block, max_splits, C.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def kvq_attend_packed_split(layout: Layout, block: int, q: torch.Tensor, k_cache, v_cache,
+                            out: torch.Tensor, workspace: torch.Tensor, max_splits: int = 8,
+                            scale: float = 0.0, stream=None) -> None:
+    """kvq_attend_packed with the key prefix cut into up to max_splits ranges;
+    workspace: a device tensor of at least kvq_attend_split_workspace() bytes."""
+    shp = _block_shape(layout, block)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("kvq_attend_packed_split",
+           lib().kvq_attend_packed_split(C.byref(layout), block, _dev(q, "q", torch.bfloat16, shp),
+                                         _cache(layout, k_cache, "k_cache"),
+                                         _cache(layout, v_cache, "v_cache"), float(scale),
+                                         _dev(out, "out", torch.float32, shp), max_splits,
+                                         _dev(workspace, "workspace"), nbytes, _stream(stream)))
 
 
 def kvq_quantize_attend(layout: Layout, block: int, k_src: torch.Tensor, v_src: torch.Tensor,
