@@ -193,7 +193,7 @@ int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q
  * exact attention within the same 2e-3 bound.
  *   max_splits  1..64, an upper bound: blocks of at most 128 queries, short
  *               prefixes (fewer than 16 key tiles per range) and grids that
- *               already hold about eight workgroups per CU use fewer ranges,
+ *               already hold about four workgroups per CU use fewer ranges,
  *               down to one (then this is exactly kvq_attend_packed)
  *   workspace   caller-owned device memory of at least workspace_bytes >=
  *               kvq_attend_split_workspace(layout, block, max_splits) bytes,

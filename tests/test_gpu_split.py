@@ -35,7 +35,8 @@ def split_and_plain(Lg, block, q_np, kg, vg, max_splits, scale=0.0):
 
 def test_video_frames_split(oracle):
     """Next-frame video shape, 3 frames of 1560 tokens: the last frame's 1560
-    queries over 4680 keys in 8 ranges (147 key tiles)."""
+    queries over 4680 keys (147 key tiles) in 4 ranges: 280 query tiles, about
+    four workgroups per CU."""
     wl = vi.WORKLOADS["video_16x1560_h40d128_int3"].with_(blocks=(1560, 1560, 1560))
     Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)
     q = vi.q_block(wl, 0, 2)

@@ -171,11 +171,13 @@ int make_attend_params(const kvq_layout* layout, int32_t block, const uint16_t* 
 }
 
 // Key ranges per query tile of kvq_attend_packed_split: enough workgroups for
-// about eight per CU of the 256 on a gfx950 device, at least 16 key tiles (512
+// about four per CU of the 256 on a gfx950 device, at least 16 key tiles (512
 // keys) per range, at most max_splits.  Blocks of at most 128 queries run the
-// kernels without ranges.
+// kernels without ranges.  Four per CU measured best on the next-frame video
+// shape (40 heads x 1560 queries, 280 query tiles: 4 ranges), against 2, 3, 5,
+// 6, 8 and 16: every range re-reads the queries and writes a partial output.
 constexpr int32_t kMaxSplits = 64;
-constexpr int64_t kSplitTargetWGs = 8 * 256;
+constexpr int64_t kSplitTargetWGs = 4 * 256;
 constexpr int64_t kMinSplitTiles = 16;
 
 int32_t pick_splits(const AttendParams& p, int32_t max_splits) {
