@@ -52,7 +52,7 @@ def test_video_frames_split(oracle):
     assert err <= ATTN_TOL, err
 
 
-@pytest.mark.parametrize("bits,head_dim", [(4, 64), (3, 64), (3, 128)])
+@pytest.mark.parametrize("bits,head_dim", [(4, 64), (3, 64), (4, 128), (3, 128)])
 def test_ranges_across_short_blocks(oracle, bits, head_dim):
     """The VAR schedule's ten blocks then a block of 1000 queries: key ranges
     start inside and across the short blocks (statistics change inside a

@@ -2,8 +2,10 @@
 //
 // Block-by-block decoding (VAR-Q abstract): the n_k queries of block k attend
 // to every cached token of blocks 0..k.  One workgroup owns up to 256 queries of
-// one (sequence, head); its waves own 32 queries each.  The packed prefix is
-// streamed once per workgroup in tiles of 32 keys, software-pipelined:
+// one (sequence, head); its waves own 32 queries each.  (For long prefixes the
+// same kernel can own one range of the prefix's key tiles instead, writing a
+// partial result that attend_merge_kernel combines by log-sum-exp.)  The packed
+// prefix is streamed once per workgroup in tiles of 32 keys, software-pipelined:
 //   iteration j:  issue the buffer loads of tile j+2's packed codes,
 //                 S^T of tile j from LDS (MFMA),
 //                 dequantize tile j+1 (loaded one iteration earlier) into the
