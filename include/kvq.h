@@ -18,6 +18,9 @@
  *   kvq_quantize_attend one decode step of one layer: kvq_quantize_block then
  *                       kvq_attend_packed for the same block, in one launch
  *                       where a fused kernel covers the shape;
+ *   kvq_attend_packed_split  kvq_attend_packed for long prefixes (next-frame
+ *                       video): key ranges in a caller-provided workspace,
+ *                       merged by log-sum-exp;
  *   kvq_bytes           the cache's byte accounting (host only).
  *
  * Conventions shared by every call
