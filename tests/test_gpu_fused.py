@@ -142,3 +142,52 @@ def test_fused_status_flags(oracle, src, second):
                       (-1e6, K.S_RANGE)]:
         assert run(put(kb, val), vb) & flag, val
         assert run(kb, put(vb, val)) & flag, val
+
+
+def test_fused_batch_768_sampled(oracle):
+    """The batch-768 shape (30 heads x 64, INT3; 23040 (sequence, head) pairs
+    per launch, the largest grids of the decode path), all ten blocks through
+    the fused call on device-drawn inputs.  The inputs of three sequences are
+    copied back for the oracle: their caches are bit-exact and sampled output
+    rows of blocks 7 and 10 are within the attention tolerance."""
+    wl = vi.WORKLOADS["var_w1920_b768_int3"]
+    Lg, _ = layouts(oracle, wl)
+    seqs = [0, 383, 767]
+    Lo = oracle.layout_of(wl, batch=len(seqs))
+    kf, vf = K.alloc_cache(Lg), K.alloc_cache(Lg)
+    ko, vo = oracle.alloc_cache(Lo), oracle.alloc_cache(Lo)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(wl.seed)
+    sel = torch.tensor(seqs, dtype=torch.int64, device=DEV)
+    rng = np.random.default_rng(3)
+
+    def host_bf16(t):
+        return np.ascontiguousarray(t.index_select(0, sel).view(torch.int16).cpu().numpy()
+                                    .view(np.uint16))
+
+    for j in range(len(wl.blocks)):
+        kb = vi.torch_block(wl, 0, "k", j, DEV, gen)
+        vb = vi.torch_block(wl, 0, "v", j, DEV, gen)
+        qb = vi.torch_block(wl, 0, "q", j, DEV, gen)
+        out = torch.full(tuple(qb.shape), float("nan"), dtype=torch.float32, device=DEV)
+        K.kvq_quantize_attend(Lg, j, kb, vb, qb, kf, vf, out)
+        torch.cuda.synchronize()
+        assert oracle.quantize_block(Lo, j, host_bf16(kb), host_bf16(vb), ko, vo) == 0
+        if j in (6, 9):
+            q_host = host_bf16(qb)
+            got = out.index_select(0, sel).cpu().numpy()
+            n = wl.blocks[j]
+            picks = [(int(rng.integers(len(seqs))), int(rng.integers(n)), int(rng.integers(wl.heads)))
+                     for _ in range(40)]
+            picks += [(len(seqs) - 1, n - 1, wl.heads - 1), (0, 0, 0)]
+            ref = np.stack([oracle.attend_row(Lo, j, q_host, ko, vo, b, i, h) for b, i, h in picks])
+            g = np.stack([got[b, i, h] for b, i, h in picks])
+            err = float(np.abs(g - ref).max() / np.abs(ref).max())
+            assert err <= ATTN_TOL, (j, err)
+        del kb, vb, qb, out
+    for dev_cache, ref in ((kf, ko), (vf, vo)):
+        got = {key: t.index_select(0, sel) for key, t in dev_cache.items()}
+        for key in ("codes", "zero", "scale"):
+            g = got[key].cpu().numpy() if key == "codes" else \
+                got[key].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(g, ref[key]), key
