@@ -185,8 +185,9 @@ int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q
 
 /*
  * kvq_attend_packed_split -- kvq_attend_packed for long prefixes and few query
- * tiles (next-frame video: 40 heads x 1560 queries over up to 16 frames of
- * 1560 keys), where one workgroup per (sequence, head, 256 queries) leaves
+ * tiles (VAR-Q abstract: next-frame prediction decodes whole frames block by
+ * block over a growing prefix; here 40 heads x 1560 queries over up to 16
+ * frames of 1560 keys), where one workgroup per (sequence, head, 256 queries) leaves
  * most of the GPU idle in the grid's last round.  The key prefix of every
  * query tile is cut into up to max_splits ranges of whole 32-key tiles; each
  * range is attended by its own workgroup into a partial result (unnormalized
