@@ -34,7 +34,8 @@ def test_tiny_last_scale(oracle):
 
 
 @pytest.mark.parametrize("name", ["var256_tiny_int4", "var_d20_b128_int4",
-                                  "var_d20_b128_int3_rope", "var_d24_b128_int4"])
+                                  "var_d20_b128_int3_rope", "var_d24_b128_int4",
+                                  "var_d24_b128_int3", "var_w1920_b768_int3"])
 def test_every_scale(oracle, name):
     wl = vi.WORKLOADS[name]
     if wl.batch > 2:

@@ -13,7 +13,7 @@ import torch
 
 import varq_inputs as vi
 import visual_autoregressive_kv_amd as K
-from gpu_common import ATTN_TOL, DEV, attn_err, fill_both, layouts, to_dev
+from gpu_common import ATTN_TOL, DEV, assert_cache_equal, attn_err, fill_both, layouts, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,31 @@ def test_video_frames_split(oracle):
     g = np.stack([got[b, i, h] for b, i, h in picks])
     err = float(np.abs(g - ref).max() / np.abs(ref).max())
     assert err <= ATTN_TOL, err
+
+
+def test_video_sixteen_frames_sampled(oracle):
+    """The video shape in full, as the decode benchmark runs it: 16 frames of
+    1560 tokens, the packed cache bit-exact against the oracle, then frame 8
+    (12480 keys) and frame 16 (24960 keys, 780 key tiles) through
+    kvq_attend_packed_split with max_splits 8 (4 ranges per query tile) on
+    sampled rows against the binary64 oracle, and close to kvq_attend_packed
+    everywhere."""
+    wl = vi.WORKLOADS["video_16x1560_h40d128_int3"]
+    Lg, Lo, kg, vg, ko, vo = fill_both(oracle, wl)
+    assert_cache_equal(kg, ko, "video K")
+    assert_cache_equal(vg, vo, "video V")
+    rng = np.random.default_rng(16)
+    for block in (7, 15):
+        q = vi.q_block(wl, 0, block)
+        got, plain = split_and_plain(Lg, block, q, kg, vg, 8)
+        assert np.isfinite(got).all()
+        assert attn_err(got, plain.astype(np.float64)) <= SPLIT_VS_PLAIN, block
+        picks = [(0, int(rng.integers(1560)), int(rng.integers(40))) for _ in range(48)]
+        picks += [(0, 1559, 39), (0, 0, 0), (0, 1536, 20)]
+        ref = np.stack([oracle.attend_row(Lo, block, q, ko, vo, b, i, h) for b, i, h in picks])
+        g = np.stack([got[b, i, h] for b, i, h in picks])
+        err = float(np.abs(g - ref).max() / np.abs(ref).max())
+        assert err <= ATTN_TOL, (block, err)
 
 
 @pytest.mark.parametrize("bits,head_dim", [(4, 64), (3, 64), (4, 128), (3, 128)])
