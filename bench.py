@@ -126,10 +126,10 @@ def measured_traffic(kernel: str, workload: str):
 
 def cpu_baseline(wl, target_s: float):
     """The oracle as it stands, on the host's cores: quantize + pack every block
-    and attend every block's queries for a sample of sequences of one layer.
-    Threads each take whole sequences (the oracle itself is single-threaded)."""
-    import numpy as np
-
+    and attend every block's queries, for a sample of (layer, sequence) pairs
+    taken in order (all sequences of layer 0, then layer 1, ...), sized to about
+    target_s seconds.  Threads each take whole pairs (the oracle itself is
+    single-threaded); inputs are generated before the clock starts."""
     import varq_inputs as vi
     from oracle import binding as ob
 
@@ -138,43 +138,63 @@ def cpu_baseline(wl, target_s: float):
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = max(1, min(cores, 16))
-    # calibrate on one sequence, then size the sample to about target_s
-    def run_seqs(seqs):
-        sub = wl.with_(batch=1)
-        Lo = ob.layout_of(sub)
-        data = []
-        for b in seqs:
-            kv = [(vi.kv_block(wl, 0, "k", j, [b]), vi.kv_block(wl, 0, "v", j, [b]),
-                   vi.q_block(wl, 0, j, [b])) for j in range(len(wl.blocks))]
-            data.append(kv)
-        def work(items, out):
-            for kv in items:
+    Lo = ob.layout_of(wl.with_(batch=1))
+
+    def run_pairs(pairs):
+        chunks = [c for c in (pairs[i::threads] for i in range(threads)) if c]
+        ready = threading.Barrier(len(chunks) + 1)
+        errors = []
+
+        def work(items):
+            try:
+                data = [[(vi.kv_block(wl, l, "k", j, [b]), vi.kv_block(wl, l, "v", j, [b]),
+                          vi.q_block(wl, l, j, [b])) for j in range(len(wl.blocks))]
+                        for l, b in items]
+            except BaseException as e:  # release the others instead of leaving them waiting
+                errors.append(e)
+                ready.abort()
+                return
+            try:
+                ready.wait()
+            except threading.BrokenBarrierError:
+                return
+            for kv in data:
                 kc, vc = ob.alloc_cache(Lo), ob.alloc_cache(Lo)
                 for j, (kb, vb, qb) in enumerate(kv):
                     ob.quantize_block(Lo, j, kb, vb, kc, vc)
                     ob.attend(Lo, j, qb, kc, vc)
-            out.append(len(items))
-        chunks = [data[i::threads] for i in range(threads)]
-        done = []
-        t0 = time.perf_counter()
-        ths = [threading.Thread(target=work, args=(c, done)) for c in chunks if c]
+
+        ths = [threading.Thread(target=work, args=(c,)) for c in chunks]
         for t in ths:
             t.start()
+        try:
+            ready.wait()
+        except threading.BrokenBarrierError:
+            pass
+        t0 = time.perf_counter()
         for t in ths:
             t.join()
+        if errors:
+            raise errors[0]
         return time.perf_counter() - t0, len(ths)
 
-    t1, _ = run_seqs([0])
-    n_seq = int(max(1, min(wl.batch, round(target_s * threads / max(t1, 1e-3)))))
-    n_seq = max(threads, (n_seq // threads) * threads) if n_seq >= threads else n_seq
-    n_seq = min(n_seq, wl.batch)
-    secs, used = run_seqs(list(range(n_seq)))
-    tokens = n_seq * wl.total_tokens  # query tokens of one layer
+    # calibrate on one pair, then size the sample to about target_s
+    t1, _ = run_pairs([(0, 0)])
+    total = wl.layers * wl.batch
+    n = int(max(1, round(target_s * threads / max(t1, 1e-3))))
+    if n >= threads:
+        n = (n // threads) * threads
+    n = min(n, total)
+    pairs = [(l, b) for l in range(wl.layers) for b in range(wl.batch)][:n]
+    secs, used = run_pairs(pairs)
+    layers = (n + wl.batch - 1) // wl.batch
+    tokens = n * wl.total_tokens  # query tokens, summed over the sampled layers
     return {"value": tokens / secs, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"1 of {wl.layers} layers, {n_seq} of {wl.batch} sequences, all "
-                      f"{len(wl.blocks)} scales (quantize+pack then attend each block), "
-                      f"{secs:.1f} s on {used} threads; tokens/s = query tokens x layers "
-                      f"per second, same unit as value"}
+            "sample": f"{n} (layer, sequence) pairs of {total}: sequences in order over "
+                      f"{layers} of {wl.layers} layers, all {len(wl.blocks)} scales "
+                      f"(quantize+pack then attend each block), {secs:.1f} s on {used} "
+                      f"threads; tokens/s = query tokens x layers per second, same unit "
+                      f"as value"}
 
 
 # ---------------------------------------------------------------------------
