@@ -174,9 +174,16 @@ int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_ro
  *   q_bf16   [B][n_k][H][D] bfloat16 bit patterns
  *   scale    softmax scale; <= 0 selects 1/sqrt(D)
  *   out      [B][n_k][H][D] fp32
- * Accuracy: max|out - exact| <= 2e-3 * max|exact| per call on VAR-shaped data
- * (QK^T as two bf16 MFMA products of a hi/lo split of k_hat, P and v_hat in
- * fp16, fp32 accumulation and softmax).
+ * Accuracy: max|out - exact| <= 2e-3 * max|exact|, per call and within every
+ * (sequence, head), where exact is the binary64 attention over the same
+ * dequantized values.  Arithmetic: QK^T as two bf16 MFMA products of a hi/lo
+ * split of k_hat (k_hat to about 2^-17 relative), P and v_hat in fp16 (v_hat
+ * formed at half scale when a V group's grid top z + L*s lies above 65504, so
+ * it never overflows), fp32 accumulation and softmax.  The bound covers every
+ * value the quantizer accepts (|x| <= 65504) as long as each score's absolute
+ * sum scale * sum_d |q_d * k_hat_d| stays below about 100 (about 30 on
+ * VAR-shaped data): a score carries an absolute error of order 2^-17 of that
+ * sum, which the softmax turns into a relative error of the weights.
  * Errors as kvq_quantize_block.
  */
 int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,

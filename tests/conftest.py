@@ -36,3 +36,25 @@ def compile_c_helper(src: str, out_dir) -> str:
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", out, src,
                     "-lm"], check=True)
     return out
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst attention errors of the GPU parity tests, per case family: per call,
+    per (sequence, head) (both asserted <= 2e-3) and per channel (reported)."""
+    gc = sys.modules.get("gpu_common")
+    if gc is None or not gc.ERR_LOG:
+        return
+    fam = {}
+    for what, e, ebh, ech in gc.ERR_LOG:
+        key = what.split(" block")[0].split(",")[0]
+        w = fam.setdefault(key, [0, 0.0, 0.0, None])
+        w[0] += 1
+        w[1], w[2] = max(w[1], e), max(w[2], ebh)
+        if ech is not None:
+            w[3] = ech if w[3] is None else max(w[3], ech)
+    tr = terminalreporter
+    tr.write_line(f"attention error vs the binary64 oracle ({len(gc.ERR_LOG)} checks; bound 2e-3 "
+                  "per call and per (b,h); per channel reported only):")
+    for key, (n, e, ebh, ech) in sorted(fam.items()):
+        ch = "sampled" if ech is None else f"{ech:.2e}"
+        tr.write_line(f"  {key:<48} n={n:<3} per call {e:.2e}  per (b,h) {ebh:.2e}  per channel {ch}")

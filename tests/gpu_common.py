@@ -7,7 +7,11 @@ import varq_inputs as vi
 import visual_autoregressive_kv_amd as K
 
 DEV = "cuda"
-ATTN_TOL = 2e-3  # max|gpu - oracle| / max|oracle| per call
+ATTN_TOL = 2e-3  # max|gpu - oracle| / max|oracle|, per call and per (sequence, head)
+
+# (case, per-call error, per-(b,h) error, per-channel error or None) of every
+# attention check in this session; conftest.py prints the worst at the end
+ERR_LOG = []
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
@@ -55,4 +59,57 @@ def assert_cache_equal(g, o, what=""):
 
 
 def attn_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max|got - ref| / max|ref| over one call's output [B][n][H][D]."""
     return float(np.abs(got.astype(np.float64) - ref).max() / np.abs(ref).max())
+
+
+def attn_err_bh(got: np.ndarray, ref: np.ndarray) -> float:
+    """The same error normalized within each (sequence, head): the largest over
+    (b, h) of max_{i,d}|got - ref| / max_{i,d}|ref| (output [B][n][H][D])."""
+    d = np.abs(got.astype(np.float64) - ref).max(axis=(1, 3))
+    m = np.abs(ref).max(axis=(1, 3))
+    return float((d / np.maximum(m, np.finfo(np.float64).tiny)).max())
+
+
+def attn_err_channel(got: np.ndarray, ref: np.ndarray) -> float:
+    """Normalized within each (sequence, head, channel): max over (b, h, d) of
+    max_i|got - ref| / max_i|ref|.  It sees the ordinary channels, whose values
+    are one to two orders of magnitude below the massive-value channels that
+    set the per-(b, h) scale.  Reported, not asserted: the pages fix no bound for it."""
+    d = np.abs(got.astype(np.float64) - ref).max(axis=1)
+    m = np.abs(ref).max(axis=1)
+    return float((d / np.maximum(m, np.finfo(np.float64).tiny)).max())
+
+
+def check_attn(got: np.ndarray, ref: np.ndarray, what: str = "", tol: float = ATTN_TOL):
+    """Assert the 2e-3 bound per call and per (sequence, head); print the per-call,
+    per-(b, h) and per-channel errors.  Returns (per call, per (b, h), per channel)."""
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    e, ebh, ech = attn_err(got, ref), attn_err_bh(got, ref), attn_err_channel(got, ref)
+    print(f"[attn] {what}: err per call {e:.2e}, per (b,h) {ebh:.2e}, per channel {ech:.2e}",
+          flush=True)
+    ERR_LOG.append((what, e, ebh, ech))
+    assert e <= tol, (what, e)
+    assert ebh <= tol, (what, "per (b,h)", ebh)
+    return e, ebh, ech
+
+
+def check_rows(got_rows: np.ndarray, ref_rows: np.ndarray, picks, what: str = "",
+               tol: float = ATTN_TOL):
+    """Sampled output rows (one (b, i, h) per pick) against single-row oracle
+    evaluations: the per-call bound over the sample, and the per-(b, h) bound with
+    each (b, h) normalized by the largest |ref| among its sampled rows (no larger
+    than the whole (b, h)'s, so the check is at least as strict)."""
+    assert np.isfinite(got_rows).all(), f"{what}: non-finite output"
+    d = np.abs(got_rows.astype(np.float64) - ref_rows)
+    e = float(d.max() / np.abs(ref_rows).max())
+    groups = {}
+    for r, (b, _, h) in enumerate(picks):
+        groups.setdefault((b, h), []).append(r)
+    ebh = max(float(d[rows].max() / np.abs(ref_rows[rows]).max()) for rows in groups.values())
+    print(f"[attn] {what}: sampled rows {len(picks)}, err per call {e:.2e}, per (b,h) {ebh:.2e}",
+          flush=True)
+    ERR_LOG.append((what, e, ebh, None))
+    assert e <= tol, (what, e)
+    assert ebh <= tol, (what, "per (b,h)", ebh)
+    return e, ebh

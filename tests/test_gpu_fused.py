@@ -8,8 +8,7 @@ import torch
 
 import varq_inputs as vi
 import visual_autoregressive_kv_amd as K
-from gpu_common import (ATTN_TOL, DEV, assert_cache_equal, attn_err, layouts,
-                        to_dev)
+from gpu_common import DEV, assert_cache_equal, check_attn, check_rows, layouts, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +55,7 @@ def test_fused_matches_two_calls_and_oracle(oracle, wl):
     for j, of, os_, ref in steps:
         assert np.isfinite(of).all(), j
         assert np.array_equal(of.view(np.uint32), os_.view(np.uint32)), j
-        assert attn_err(of, ref) <= ATTN_TOL, j
+        check_attn(of, ref, f"fused {wl.name} block {j}")
 
 
 def test_fused_explicit_scale(oracle):
@@ -64,7 +63,7 @@ def test_fused_explicit_scale(oracle):
     *_, steps = decode_both_ways(oracle, wl, scale=0.07)
     for j, of, os_, ref in steps:
         assert np.array_equal(of.view(np.uint32), os_.view(np.uint32)), j
-        assert attn_err(of, ref) <= ATTN_TOL, j
+        check_attn(of, ref, f"fused explicit scale block {j}")
 
 
 def test_fused_full_batch_every_block(oracle):
@@ -100,8 +99,7 @@ def test_fused_full_batch_every_block(oracle):
             picks += [(127, n - 1, 19), (0, 0, 0)]
             ref = np.stack([oracle.attend_row(Lo, j, q_np, ko, vo, b, i, h) for b, i, h in picks])
             g = np.stack([got[b, i, h] for b, i, h in picks])
-            err = float(np.abs(g - ref).max() / np.abs(ref).max())
-            assert err <= ATTN_TOL, (j, err)
+            check_rows(g, ref, picks, f"fused d20 batch 128 block {j}")
     for a, b in ((kf, ks), (vf, vs)):
         for key in ("codes", "zero", "scale"):
             assert torch.equal(a[key], b[key]), key
@@ -182,8 +180,7 @@ def test_fused_batch_768_sampled(oracle):
             picks += [(len(seqs) - 1, n - 1, wl.heads - 1), (0, 0, 0)]
             ref = np.stack([oracle.attend_row(Lo, j, q_host, ko, vo, b, i, h) for b, i, h in picks])
             g = np.stack([got[b, i, h] for b, i, h in picks])
-            err = float(np.abs(g - ref).max() / np.abs(ref).max())
-            assert err <= ATTN_TOL, (j, err)
+            check_rows(g, ref, picks, f"fused batch 768 block {j}")
         del kb, vb, qb, out
     for dev_cache, ref in ((kf, ko), (vf, vo)):
         got = {key: t.index_select(0, sel) for key, t in dev_cache.items()}

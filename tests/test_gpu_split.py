@@ -13,7 +13,8 @@ import torch
 
 import varq_inputs as vi
 import visual_autoregressive_kv_amd as K
-from gpu_common import ATTN_TOL, DEV, assert_cache_equal, attn_err, fill_both, layouts, to_dev
+from gpu_common import (ATTN_TOL, DEV, assert_cache_equal, attn_err, check_attn, check_rows,
+                        fill_both, layouts, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,8 +49,7 @@ def test_video_frames_split(oracle):
     picks += [(0, 1559, 39), (0, 1536, 0), (0, 0, 0), (0, 255, 7), (0, 256, 8)]
     ref = np.stack([oracle.attend_row(Lo, 2, q, ko, vo, b, i, h) for b, i, h in picks])
     g = np.stack([got[b, i, h] for b, i, h in picks])
-    err = float(np.abs(g - ref).max() / np.abs(ref).max())
-    assert err <= ATTN_TOL, err
+    check_rows(g, ref, picks, "video frame 3, key ranges")
 
 
 def test_video_sixteen_frames_sampled(oracle):
@@ -73,8 +73,7 @@ def test_video_sixteen_frames_sampled(oracle):
         picks += [(0, 1559, 39), (0, 0, 0), (0, 1536, 20)]
         ref = np.stack([oracle.attend_row(Lo, block, q, ko, vo, b, i, h) for b, i, h in picks])
         g = np.stack([got[b, i, h] for b, i, h in picks])
-        err = float(np.abs(g - ref).max() / np.abs(ref).max())
-        assert err <= ATTN_TOL, (block, err)
+        check_rows(g, ref, picks, f"video frame {block + 1}, key ranges")
 
 
 @pytest.mark.parametrize("bits,head_dim", [(4, 64), (3, 64), (4, 128), (3, 128)])
@@ -92,7 +91,7 @@ def test_ranges_across_short_blocks(oracle, bits, head_dim):
         got, plain = split_and_plain(Lg, last, q, kg, vg, max_splits, scale=0.09)
         assert attn_err(got, plain.astype(np.float64)) <= SPLIT_VS_PLAIN, max_splits
         got_def, _ = split_and_plain(Lg, last, q, kg, vg, max_splits)
-        assert attn_err(got_def, ref) <= ATTN_TOL, max_splits
+        check_attn(got_def, ref, f"key ranges INT{bits} D={head_dim} max_splits {max_splits}")
 
 
 def test_one_range_is_kvq_attend_packed(oracle):

@@ -189,3 +189,15 @@ def test_quantize_block_matches_groupwise(oracle):
                 assert kc["zero"][b, h, k, d] == z and kc["scale"][b, h, k, d] == s
                 tile[:, d] = codes
             assert np.array_equal(kc["codes"][b, h, off:off + n], oracle.pack(3, tile))
+
+
+def test_edge_groups_top_level_exceeds_binary16(oracle):
+    """In-range binary32 groups whose top grid level z + L*s exceeds the binary16
+    maximum (the premise of tests/test_gpu_range.py): the statistics are
+    binary16, the grid top is not."""
+    for bits, vals, top in [(4, [0.0, 65504.0], 65520.0), (4, [-65504.0, 65504.0], 65536.0),
+                            (3, [0.0, 65504.0], 65520.0)]:
+        st, zb, sb, _ = oracle.quantize_group(np.array(vals, np.float32), bits)
+        assert st == 0
+        z, s = float(oracle.h2f(np.array([zb]))[0]), float(oracle.h2f(np.array([sb]))[0])
+        assert z + ((1 << bits) - 1) * s == top, (bits, vals, z, s)

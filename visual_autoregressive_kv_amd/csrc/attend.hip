@@ -97,6 +97,20 @@ __device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
                                             false);
 }
 
+// Whether the top grid level z + L*s of any of 8 value groups can leave the
+// binary16 range.  Binary32 input up to +-65504 can give a top level of up to
+// about 65566 after the step is rounded up; the attention then forms v_hat / 2
+// in binary16 (exact halving) and doubles its output, so v_hat never overflows.
+template <int BITS>
+__device__ __forceinline__ bool v_top_over_f16(const u32x4& zw, const u32x4& sw) {
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  const f16x8 z = __builtin_bit_cast(f16x8, zw), s = __builtin_bit_cast(f16x8, sw);
+  bool over = false;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) over |= __builtin_fmaf(LEVELS, (float)s[c], (float)z[c]) > 65504.0f;
+  return over;
+}
+
 // the 8 codes of one packed chunk as fp32
 template <int BITS>
 __device__ __forceinline__ void codes_f32(uint32_t w, float c[8]) {
@@ -144,7 +158,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* prefi
 // ---------------------------------------------------------------------------
 template <int D, int BITS, int NW, bool CHECK>
 __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, int h, int tid,
-                                                  _Float16* st_lds, float* scratch) {
+                                                  _Float16* st_lds, float* scratch, int& vover) {
   static_assert(D == kWave && NW >= 2, "64-channel heads, at least one wave per tensor");
   constexpr int CPR = D / 8;
   constexpr int GT = NW * kWave / 2;  // threads per tensor
@@ -229,6 +243,7 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     srow[D + ch] = __builtin_bit_cast(_Float16, gst.sb);
     zi[(tensor * 2 + 0) * kWave + ch] = gst.zf;
     zi[(tensor * 2 + 1) * kWave + ch] = gst.inv;
+    if (tensor == 1) vover |= __builtin_fmaf(LEVELS, h2f(gst.sb), gst.zf) > 65504.0f;
   }
   __syncthreads();
   float zf[8], inv[8];
@@ -314,9 +329,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   // Fused launch: quantize block k first (k_hi is free until tile 0 is
   // dequantized; the statistics slot of block k in LDS is filled here, the
   // copy below skips it; the barrier after the copy publishes everything).
+  int vover = 0;  // a V group's top grid level leaves the binary16 range
   if constexpr (FUSE != 0) {
     quantize_block_wg<D, BITS, NW, FUSE == 2>(p, b, h, tid, st,
-                                              reinterpret_cast<float*>(&k_hi[0][0][0]));
+                                              reinterpret_cast<float*>(&k_hi[0][0][0]), vover);
   }
 
   // ---- item slots: (tensor, key, chunk), fixed for every tile ----------------
@@ -370,10 +386,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       const int cg = rem - tensor * CPR;
       const int64_t gi = stat_base + (int64_t)blk * D + 8 * cg;
       _Float16* row = st + ((blk * 2 + tensor) * 2) * D + 8 * cg;
-      *reinterpret_cast<u32x4*>(row) =
-          *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kzero : p.vzero) + gi);
-      *reinterpret_cast<u32x4*>(row + D) =
-          *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kscale : p.vscale) + gi);
+      const u32x4 zw = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kzero : p.vzero) + gi);
+      const u32x4 sw = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kscale : p.vscale) + gi);
+      *reinterpret_cast<u32x4*>(row) = zw;
+      *reinterpret_cast<u32x4*>(row + D) = sw;
+      if (tensor == 1) vover |= v_top_over_f16<BITS>(zw, sw);
     }
   }
   bf16x8 qop[KS];
@@ -386,7 +403,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       qop[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __syncthreads();  // blk_end, statistics and (fused) block k's rows visible
+  // blk_end, statistics and (fused) block k's rows visible; every workgroup of
+  // a (sequence, head) sees the same statistics, so key ranges agree on vhalf
+  const bool vhalf = __syncthreads_or(vover) != 0;
   if (!early0) issue_loads(j_begin, preA, pre2A);
   issue_loads(j_begin + 1, preB, pre2B);  // no records past the prefix: reads nothing
 
@@ -435,6 +454,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       codes_f32<BITS>(w, cf);
 #pragma unroll
       for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]);
+      if (s_tensor[i] != 0 && vhalf) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] *= 0.5f;
+      }
       if (s_tensor[i] == 0) {
         u32x4 hi, lo;
 #pragma unroll
@@ -581,8 +604,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   if (j < j_end) step(j, preB, pre2B, preA, pre2A);
 
   const float l_tot = sum_xor32(l_run);
+  const float oscale = vhalf ? 2.0f : 1.0f;  // undo the v_hat halving
   if constexpr (SPLIT) {
     // ---- partial result of this key range: O unnormalized, m c, l ----------
+#pragma unroll
+    for (int i = 0; i < MT; ++i) o[i] *= oscale;
     if (q_ok) {
       const int64_t row = ((int64_t)b * p.n + q) * p.H + h;
       float* orow = p.ws_o + ((int64_t)sp * p.ws_rows + row) * D;
@@ -603,7 +629,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   }
 
   // ---- normalize and store (fp32) ----------------------------------------
-  const float inv_l = 1.0f / l_tot;
+  const float inv_l = oscale / l_tot;
   if (q_ok) {
     float* orow = p.out + (((int64_t)b * p.n + q) * p.H + h) * D;
 #pragma unroll
@@ -637,7 +663,7 @@ constexpr int kFusedRowBytes = 32;  // LDS bytes per packed row of the fused blo
 template <int D, int BITS, bool F32, bool CHECK>
 __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b, int h, int lane,
                                                     _Float16* st_lds, uint8_t* rows_lds,
-                                                    float* scratch) {
+                                                    float* scratch, int& vover) {
   static_assert(D == kWave, "the wave quantizer covers 64-channel heads, one channel per lane");
   constexpr int CPR = D / 8;
   constexpr int TL = kWave / CPR;  // token lanes of phase 2
@@ -676,6 +702,7 @@ __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b
     srow[D + lane] = __builtin_bit_cast(_Float16, gst.sb);
     scratch[lane] = gst.zf;
     scratch[D + lane] = gst.inv;
+    if (tensor == 1) vover |= __builtin_fmaf(LEVELS, h2f(gst.sb), gst.zf) > 65504.0f;
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     // ---- phase 2: codes of (token, 8-channel chunk) items
     const int cg = lane % CPR;
@@ -820,6 +847,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   // the launcher only picks this kernel when every statistic fits the wave's
   // LDS; a fused launch writes block k's own statistics there itself
   const int nkb_copy = FUSE != 0 ? nkb - 1 : nkb;
+  int vover = 0;  // a V group's top grid level leaves the binary16 range
   for (int i = lane; i < nkb_copy * 2 * CPR; i += kWave) {
     const int blk = i / (2 * CPR);
     const int rem = i - blk * 2 * CPR;
@@ -827,10 +855,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
     const int cg = rem - tensor * CPR;
     const int64_t gi = stat_base + (int64_t)blk * D + 8 * cg;
     _Float16* row = st + ((blk * 2 + tensor) * 2) * D + 8 * cg;
-    *reinterpret_cast<u32x4*>(row) =
-        *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kzero : p.vzero) + gi);
-    *reinterpret_cast<u32x4*>(row + D) =
-        *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kscale : p.vscale) + gi);
+    const u32x4 zw = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kzero : p.vzero) + gi);
+    const u32x4 sw = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.kscale : p.vscale) + gi);
+    *reinterpret_cast<u32x4*>(row) = zw;
+    *reinterpret_cast<u32x4*>(row + D) = sw;
+    if (tensor == 1) vover |= v_top_over_f16<BITS>(zw, sw);
   }
   if (lane < nkb) bend[lane] = p.block_end[lane];
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -853,7 +882,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   const uint8_t* qrows = rows_all[wave];
   if constexpr (FUSE != 0)
     quantize_block_wave<D, BITS, FUSE >= 3, FUSE == 2 || FUSE == 4>(
-        p, b, h, lane, st, rows_all[wave], reinterpret_cast<float*>(&v_t[0][0]));
+        p, b, h, lane, st, rows_all[wave], reinterpret_cast<float*>(&v_t[0][0]), vover);
+  const bool vhalf = __any(vover);
 
   // Every K and V item of a lane is key `col` of the tile, so one block index
   // per lane follows the tiles; it only moves forward.
@@ -937,6 +967,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
       codes_f32<BITS>(bits_of(vc[i], v_shift[i]), cf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
+      if (vhalf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= 0.5f;
+      }
       const uint32_t h01 = pk_f16(x[0], x[1]), h23 = pk_f16(x[2], x[3]);
       const uint32_t h45 = pk_f16(x[4], x[5]), h67 = pk_f16(x[6], x[7]);
       const bool odd = v_key[i] & 1;
@@ -1043,7 +1077,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   // ---- normalize and store (fp32) ----------------------------------------
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float inv_l = 1.0f / sum_xor32(l_run[qt]);
+    const float inv_l = (vhalf ? 2.0f : 1.0f) / sum_xor32(l_run[qt]);
     const int q = 32 * qt + col;
     if (q < p.n) {
       float* orow = p.out + (((int64_t)b * p.n + q) * p.H + h) * D;
