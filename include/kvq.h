@@ -223,6 +223,34 @@ int kvq_attend_packed_split(const kvq_layout* layout, int32_t block, const uint1
 int kvq_attend_split_workspace(const kvq_layout* layout, int32_t block, int32_t max_splits,
                                uint64_t* bytes);
 
+/* size of the static device scratch array of kvq_attend_packed_split_noalloc:
+ * one copy per GPU the library runs on, held until the process ends (128 MiB:
+ * a next-frame video frame of 40 heads x 1560 queries at head_dim 128 in 4 key
+ * ranges needs 124 MiB) */
+#define KVQ_STATIC_SCRATCH_BYTES (128ull << 20)
+
+/*
+ * kvq_attend_packed_split_noalloc -- kvq_attend_packed_split for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the key ranges' partials live in
+ * the library's static device array of KVQ_STATIC_SCRATCH_BYTES on the current
+ * GPU instead of a caller workspace.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); on its first use on a GPU it looks up that
+ * GPU's copy of the array once.  Outputs equal kvq_attend_packed_split's with
+ * the same layout, block, inputs, scale and max_splits.
+ *   Errors as kvq_attend_packed_split; KVQ_E_INVAL also when
+ *   kvq_attend_split_workspace(layout, block, max_splits) exceeds
+ *   KVQ_STATIC_SCRATCH_BYTES (lower max_splits, or use the workspace call).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call writes every partial before it reads it, so nothing is
+ * cleared): calls ordered on one stream are safe, calls that overlap in time
+ * on one GPU (several streams, or host threads without ordering) race.
+ */
+int kvq_attend_packed_split_noalloc(const kvq_layout* layout, int32_t block,
+                                    const uint16_t* q_bf16, kvq_cache_const k_cache,
+                                    kvq_cache_const v_cache, float scale, float* out,
+                                    int32_t max_splits, hipStream_t stream);
+
 /*
  * kvq_quantize_attend -- the decode step of one layer for block k (VAR-Q
  * abstract: the block is quantized when the generation loop hands it over,

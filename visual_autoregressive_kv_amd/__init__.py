@@ -7,8 +7,9 @@ functions below are its thin Python binding (torch supplies device memory and
 streams only).
 """
 from .kvq import (  # noqa: F401
-    BF16, F32, KvqError, Layout, S_NONFINITE, S_RANGE, alloc_cache, cache_shapes,
-    header_symbols, kvq_attend_packed, kvq_attend_packed_split, kvq_attend_split_workspace,
+    BF16, F32, KvqError, Layout, S_NONFINITE, S_RANGE, STATIC_SCRATCH_BYTES, alloc_cache, cache_shapes,
+    header_symbols, kvq_attend_packed, kvq_attend_packed_split, kvq_attend_packed_split_noalloc,
+    kvq_attend_split_workspace,
     kvq_bytes, kvq_dequantize, kvq_pack, kvq_quantize_attend, kvq_quantize_block,
     kvq_stream_copy, kvq_unpack, kvq_version, lib, make_layout,
 )

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -196,6 +197,29 @@ uint64_t split_workspace_bytes(const kvq_layout* L, int32_t block, int32_t split
   return (uint64_t)splits * rows * ((uint64_t)L->head_dim + 2u) * 4u;
 }
 
+// Static scratch of kvq_attend_packed_split_noalloc.  In host code `scratch`
+// is only a stand-in for the symbol: each GPU holds its own copy at its own
+// address, looked up once per device (with that device current) and kept in
+// scratch_ptr; kernels only ever see that address.
+__device__ __align__(256) uint8_t scratch[KVQ_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// device address of the current GPU's scratch array, or nullptr on failure
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+
 kvq_cache_const const_view(kvq_cache c) {
   kvq_cache_const r;
   r.codes = c.codes;
@@ -361,6 +385,26 @@ int kvq_attend_packed_split(const kvq_layout* layout, int32_t block, const uint1
   if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
   p.ws_rows = (int64_t)p.B * p.n * p.H;
   p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + (int64_t)p.splits * p.ws_rows * layout->head_dim;
+  return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream));
+}
+
+int kvq_attend_packed_split_noalloc(const kvq_layout* layout, int32_t block,
+                                    const uint16_t* q_bf16, kvq_cache_const k_cache,
+                                    kvq_cache_const v_cache, float scale, float* out,
+                                    int32_t max_splits, hipStream_t stream) {
+  AttendParams p;
+  const int rc = make_attend_params(layout, block, q_bf16, k_cache, v_cache, scale, out, &p);
+  if (rc != KVQ_OK) return rc;
+  if (max_splits < 1 || max_splits > kMaxSplits) return KVQ_E_INVAL;
+  if (split_workspace_bytes(layout, block, max_splits) > KVQ_STATIC_SCRATCH_BYTES)
+    return KVQ_E_INVAL;
+  p.splits = pick_splits(p, max_splits);
+  if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+  void* ws = device_scratch();
+  if (!ws) return KVQ_E_DEVICE;
+  p.ws_rows = (int64_t)p.B * p.n * p.H;
+  p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + (int64_t)p.splits * p.ws_rows * layout->head_dim;
   return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream));
 }

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "kvq.h")
 
 MAX_BLOCKS = 64
+STATIC_SCRATCH_BYTES = 128 << 20  # KVQ_STATIC_SCRATCH_BYTES
 OK, E_INVAL, E_UNSUPPORTED, E_DEVICE = 0, -1, -2, -3
 S_NONFINITE, S_RANGE = 1, 2
 F32, BF16 = 0, 1
@@ -91,6 +92,9 @@ def lib() -> C.CDLL:
         L.kvq_attend_packed_split.restype = C.c_int
         L.kvq_attend_packed_split.argtypes = [C.POINTER(Layout), i32, vp, Cache, Cache, C.c_float,
                                               vp, i32, vp, u64, vp]
+        L.kvq_attend_packed_split_noalloc.restype = C.c_int
+        L.kvq_attend_packed_split_noalloc.argtypes = [C.POINTER(Layout), i32, vp, Cache, Cache,
+                                                      C.c_float, vp, i32, vp]
         L.kvq_attend_split_workspace.restype = C.c_int
         L.kvq_attend_split_workspace.argtypes = [C.POINTER(Layout), i32, i32, C.POINTER(u64)]
         L.kvq_stream_copy.restype = C.c_int
@@ -280,6 +284,19 @@ def kvq_attend_packed_split(layout: Layout, block: int, q: torch.Tensor, k_cache
                                          _cache(layout, v_cache, "v_cache"), float(scale),
                                          _dev(out, "out", torch.float32, shp), max_splits,
                                          _dev(workspace, "workspace"), nbytes, _stream(stream)))
+
+
+def kvq_attend_packed_split_noalloc(layout: Layout, block: int, q: torch.Tensor, k_cache,
+                                    v_cache, out: torch.Tensor, max_splits: int = 8,
+                                    scale: float = 0.0, stream=None) -> None:
+    """kvq_attend_packed_split with the partials in the library's static device
+    scratch array (no workspace argument, no allocation)."""
+    shp = _block_shape(layout, block)
+    _check("kvq_attend_packed_split_noalloc",
+           lib().kvq_attend_packed_split_noalloc(
+               C.byref(layout), block, _dev(q, "q", torch.bfloat16, shp),
+               _cache(layout, k_cache, "k_cache"), _cache(layout, v_cache, "v_cache"),
+               float(scale), _dev(out, "out", torch.float32, shp), max_splits, _stream(stream)))
 
 
 def kvq_quantize_attend(layout: Layout, block: int, k_src: torch.Tensor, v_src: torch.Tensor,
