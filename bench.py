@@ -134,10 +134,14 @@ def cpu_baseline(wl, target_s: float):
     from oracle import binding as ob
 
     try:
-        cores = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    threads = max(1, min(cores, 16))
+        affinity = os.cpu_count() or 1
+    # every core this process may run on, unless the host caps its CPU share
+    # through OMP_NUM_THREADS (the oracle is single-threaded per pair; the
+    # threads below each take whole pairs)
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = max(1, min(affinity, share) if share > 0 else affinity)
     Lo = ob.layout_of(wl.with_(batch=1))
 
     def run_pairs(pairs):
@@ -190,11 +194,14 @@ def cpu_baseline(wl, target_s: float):
     layers = (n + wl.batch - 1) // wl.batch
     tokens = n * wl.total_tokens  # query tokens, summed over the sampled layers
     return {"value": tokens / secs, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "host_cores": {"affinity": affinity, "cpu_count": os.cpu_count(),
+                           "omp_num_threads": share or None},
             "sample": f"{n} (layer, sequence) pairs of {total}: sequences in order over "
                       f"{layers} of {wl.layers} layers, all {len(wl.blocks)} scales "
                       f"(quantize+pack then attend each block), {secs:.1f} s on {used} "
-                      f"threads; tokens/s = query tokens x layers per second, same unit "
-                      f"as value"}
+                      f"threads (host: {affinity} cores in this process's affinity mask, "
+                      f"cpu_count {os.cpu_count()}); tokens/s = query tokens x layers per "
+                      f"second, same unit as value"}
 
 
 # ---------------------------------------------------------------------------
@@ -249,7 +256,16 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     copy_gbps = 10 * 2 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del a, c
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        K.kvq_stream_read(a, sink)
+    e0.record()
+    for _ in range(10):
+        K.kvq_stream_read(a, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbps = 10 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, c, sink
 
     # pre-marshalled calls: the timed loop only crosses into the library
     stream = torch.cuda.current_stream()
@@ -263,30 +279,31 @@ def main():
     vC = [cache(x) for x in vcs]
     # Decode order: for every block, for every layer, that layer's decode step.
     # Blocks the library fuses (head_dim 64, at most FUSED_MAX_TOKENS tokens) go
-    # through kvq_quantize_attend (one launch); larger blocks through
-    # kvq_quantize_block then kvq_attend_packed (two launches).
-    def fused(j):
-        return (not args.unfused and wl.head_dim == 64 and wl.blocks[j] <= FUSED_MAX_TOKENS
+    # through kvq_quantize_attend (one launch); larger blocks, and every block of
+    # the separate-pass measurement, through kvq_quantize_block then
+    # kvq_attend_packed_split (or kvq_attend_packed with --no-split).
+    def can_fuse(j):
+        return (wl.head_dim == 64 and wl.blocks[j] <= FUSED_MAX_TOKENS
                 and (wl.src == "bf16" or wl.blocks[j] <= 32))
 
-    # workspace of kvq_attend_packed_split, sized for the largest unfused block
+    # workspace of kvq_attend_packed_split, sized for the largest block
     split = not args.no_split
-    ws_bytes = max([K.kvq_attend_split_workspace(L, j, MAX_SPLITS) for j in range(NB)
-                    if not fused(j)] or [0]) if split else 0
+    ws_bytes = max(K.kvq_attend_split_workspace(L, j, MAX_SPLITS) for j in range(NB)) if split else 0
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     ws_ptr, ws_n = ws.data_ptr(), C.c_uint64(ws.numel())
 
-    calls = []  # (kind, block, function, arguments), in launch order
-    for j in range(NB):
-        for l in range(wl.layers):
-            # shapes are fixed by construction; check them once here through the binding
-            assert tuple(Kin[l][j].shape) == (wl.batch, wl.blocks[j], wl.heads, wl.head_dim)
-            if fused(j):
-                calls.append(("fused", j, lib.kvq_quantize_attend,
-                              (Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
-                               Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
-                               Out[l][j].data_ptr(), None, sh)))
-            else:
+    def build_calls(fuse: bool):
+        calls = []  # (kind, block, function, arguments), in launch order
+        for j in range(NB):
+            for l in range(wl.layers):
+                # shapes are fixed by construction; checked once here
+                assert tuple(Kin[l][j].shape) == (wl.batch, wl.blocks[j], wl.heads, wl.head_dim)
+                if fuse and can_fuse(j):
+                    calls.append(("fused", j, lib.kvq_quantize_attend,
+                                  (Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
+                                   Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
+                                   Out[l][j].data_ptr(), None, sh)))
+                    continue
                 calls.append(("quant_pack", j, lib.kvq_quantize_block,
                               (Lref, j, kb.BF16, Kin[l][j].data_ptr(), Vin[l][j].data_ptr(),
                                kC[l], vC[l], None, sh)))
@@ -298,18 +315,19 @@ def main():
                     calls.append(("attend", j, lib.kvq_attend_packed,
                                   (Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
                                    Out[l][j].data_ptr(), sh)))
+        return calls
+
+    calls = build_calls(fuse=not args.unfused)
     # one checked call of each kind through the binding before the raw loop
     K.kvq_quantize_block(L, 0, Kin[0][0], Vin[0][0], kcs[0], vcs[0])
     K.kvq_attend_packed(L, 0, Qin[0][0], kcs[0], vcs[0], Out[0][0])
     K.kvq_quantize_attend(L, 0, Kin[0][0], Vin[0][0], Qin[0][0], kcs[0], vcs[0], Out[0][0])
 
-    # One event per launch boundary: ev[c] before call c, ev[c + 1] after it.
-    n_calls = len(calls)
-
-    def step(events=None):
+    def step(cs, events=None):
+        """One decode step; events[c] before call c and events[c + 1] after it."""
         if events is not None:
             events[0].record(stream)
-        for c, (_, _, fn, cargs) in enumerate(calls):
+        for c, (_, _, fn, cargs) in enumerate(cs):
             rc = fn(*cargs)
             if events is not None:
                 events[c + 1].record(stream)
@@ -317,9 +335,12 @@ def main():
                 raise RuntimeError(f"kvq launch failed (rc={rc}) at call {c}")
 
     for w in range(args.warmup):
-        step()
+        step(calls)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", flush=True)
+
+    def new_events(k, steps):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(steps)]
 
     # Timed region.  When every launch of a step is of one kind (the fused VAR
     # decode step), one event pair per step gives that kind's average launch
@@ -328,28 +349,24 @@ def main():
     # every launch boundary.  Per-block spans then come from a separate pass
     # after the timed region.
     single_kind = len({c[0] for c in calls}) == 1
-
-    def new_events(k):
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(args.steps)]
-
-    evs = new_events(2 if single_kind else n_calls + 1)
+    evs = new_events(2 if single_kind else len(calls) + 1, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):
         if single_kind:
             evs[s_][0].record(stream)
-            step()
+            step(calls)
             evs[s_][1].record(stream)
         else:
-            step(evs[s_])
+            step(calls, evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     # per-launch spans: the timed events (several kinds) or a separate pass
     if single_kind:
-        span_evs = new_events(n_calls + 1)
+        span_evs = new_events(len(calls) + 1, args.steps)
         for s_ in range(args.steps):
-            step(span_evs[s_])
+            step(calls, span_evs[s_])
         torch.cuda.synchronize()
     else:
         span_evs = evs
@@ -357,17 +374,23 @@ def main():
     # per kind: summed event time, launches, algorithmic bytes and flops
     byte_model = {"quant_pack": quant_bytes, "attend": attend_bytes,
                   "fused": lambda w, k: quant_bytes(w, k) + attend_bytes(w, k)}
-    kinds = {}
-    per_block = {}
-    for c, (kind, j, _, _) in enumerate(calls):
-        ms = sum(span_evs[s_][c].elapsed_time(span_evs[s_][c + 1]) for s_ in range(args.steps))
-        k = kinds.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
-        k["ms"] += ms
-        k["launches"] += args.steps
-        k["bytes"] += byte_model[kind](wl, j) * args.steps
-        if kind in ("attend", "fused"):
-            k["flops"] += attend_flops(wl, j) * args.steps
-        per_block.setdefault(kind, {}).setdefault(j, []).append(ms / args.steps)
+
+    def kind_totals(cs, span, steps):
+        kinds, per_block = {}, {}
+        for c, (kind, j, _, _) in enumerate(cs):
+            ms = sum(span[s_][c].elapsed_time(span[s_][c + 1]) for s_ in range(steps))
+            k = kinds.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0,
+                                        "tokens": 0})
+            k["ms"] += ms
+            k["launches"] += steps
+            k["bytes"] += byte_model[kind](wl, j) * steps
+            if kind in ("attend", "fused"):
+                k["flops"] += attend_flops(wl, j) * steps
+                k["tokens"] += wl.batch * wl.blocks[j] * steps
+            per_block.setdefault(kind, {}).setdefault(j, []).append(ms / steps)
+        return kinds, per_block
+
+    kinds, per_block = kind_totals(calls, span_evs, args.steps)
     if single_kind:  # the kind's time is the timed steps' span
         only = kinds[calls[0][0]]
         only["ms"] = sum(e[0].elapsed_time(e[1]) for e in evs)
@@ -392,18 +415,55 @@ def main():
                 "traffic": traffic, "kernel": dominant,
                 "blocks": per_block_blocks[dominant],
                 "avg_launch_us": round(avg_ms * 1e3, 3),
-                "algorithmic_bytes_per_launch": round(avg_bytes)}
-    kind_stats = {}
-    for kind, k in sorted(kinds.items()):
+                "algorithmic_bytes_per_launch": round(avg_bytes),
+                "frac_of_copy_peak": round(achieved / copy_gbps, 4),
+                "frac_of_read_peak": round(achieved / read_gbps, 4)}
+
+    def stats_of(k, steps):
         g = gbps(k)
-        e = {"ms_per_step": round(k["ms"] / args.steps, 4), "GBps": round(g, 1),
-             "pct_hbm_peak": round(100 * g / HBM_PEAK_GBPS, 2),
-             "blocks": per_block_blocks[kind]}
+        e = {"ms_per_step": round(k["ms"] / steps, 4), "GBps": round(g, 1),
+             "pct_hbm_peak": round(100 * g / HBM_PEAK_GBPS, 2)}
         if k["flops"]:
             tf = k["flops"] / (k["ms"] * 1e-3) / 1e12
+            e["tokens_per_s"] = round(k["tokens"] / (k["ms"] * 1e-3), 1)  # query tokens x layers
             e["TFLOPs"] = round(tf, 2)
             e["pct_bf16_mfma_peak"] = round(100 * tf / BF16_PEAK_TFLOPS, 2)
-        kind_stats[kind] = e
+        return e
+
+    kind_stats = {}
+    for kind, k in sorted(kinds.items()):
+        kind_stats[kind] = stats_of(k, args.steps)
+        kind_stats[kind]["blocks"] = per_block_blocks[kind]
+
+    # The two passes the metric names, timed separately in the same run after
+    # the headline steps: every block as kvq_quantize_block (quantize + pack)
+    # then the attention call, events at every launch boundary.
+    passes = None
+    if "fused" in kinds:
+        sep = build_calls(fuse=False)
+        step(sep)
+        torch.cuda.synchronize()
+        sep_steps = max(1, min(args.steps, 5))
+        sep_evs = new_events(len(sep) + 1, sep_steps)
+        for s_ in range(sep_steps):
+            step(sep, sep_evs[s_])
+        torch.cuda.synchronize()
+        sk, sb = kind_totals(sep, sep_evs, sep_steps)
+        passes = {"steps": sep_steps,
+                  "timing": "events at every launch boundary (each span: the kernel plus the "
+                            "gap since the previous launch)",
+                  "quantize_pack": stats_of(sk["quant_pack"], sep_steps),
+                  "attention": stats_of(sk["attend"], sep_steps),
+                  "per_block_us": {kind: [round(1e3 * sum(v) / len(v), 2)
+                                          for _, v in sorted(d.items())]
+                                   for kind, d in sb.items()}}
+        passes["attention"]["call"] = ("kvq_attend_packed" if not split else
+                                       f"kvq_attend_packed_split (max {MAX_SPLITS} key ranges)")
+    elif "quant_pack" in kinds and "attend" in kinds:
+        passes = {"steps": args.steps, "timing": "the timed steps' events",
+                  "quantize_pack": stats_of(kinds["quant_pack"], args.steps),
+                  "attention": stats_of(kinds["attend"], args.steps)}
+
     out = {
         "metric": "packed-KV attention tokens/s + quantize/pack GB/s, % of HBM peak (1 GPU)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -414,7 +474,9 @@ def main():
                    "schedule": list(wl.blocks), "tokens_per_seq": wl.total_tokens,
                    "parallelism": "none (1 GPU)"},
         "kernels": kind_stats,
+        "passes": passes,
         "copy_peak_GBps": round(copy_gbps, 1),
+        "read_peak_GBps": round(read_gbps, 1),
         "timing": ("one event pair per timed step; per-block spans from a separate pass"
                    if single_kind else "events at every launch boundary of the timed steps"),
         "per_block_us": per_block_us,

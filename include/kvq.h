@@ -286,6 +286,12 @@ int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const c
  * HBM bandwidth and calibrates the memory counters */
 int kvq_stream_copy(const void* src, void* dst, uint64_t n_bytes, hipStream_t stream);
 
+/* plain streaming read of n_bytes (multiple of 16) into nothing: measures the
+ * achievable HBM read bandwidth (the decode passes mostly read); `sink` is a
+ * device word that is written only if the data's xor fold equals a fixed
+ * pattern, so the loads cannot be optimized away */
+int kvq_stream_read(const void* src, uint64_t n_bytes, uint32_t* sink, hipStream_t stream);
+
 /* version string of the library */
 const char* kvq_version(void);
 

@@ -11,5 +11,5 @@ from .kvq import (  # noqa: F401
     header_symbols, kvq_attend_packed, kvq_attend_packed_split, kvq_attend_packed_split_noalloc,
     kvq_attend_split_workspace,
     kvq_bytes, kvq_dequantize, kvq_pack, kvq_quantize_attend, kvq_quantize_block,
-    kvq_stream_copy, kvq_unpack, kvq_version, lib, make_layout,
+    kvq_stream_copy, kvq_stream_read, kvq_unpack, kvq_version, lib, make_layout,
 )

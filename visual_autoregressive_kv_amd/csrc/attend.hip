@@ -148,31 +148,46 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* prefi
 // Fused launch, quantize side for a workgroup that owns one (sequence, head):
 // the first half of the threads quantizes block k of K, the second half of V
 // (bf16 input, the same group statistics and code arithmetic as the standalone
-// quantize kernel).  Thread (row group rg, chunk c) of a half holds channels
-// 8 c .. 8 c + 7 of rows rg, rg + RG, .. (at most 8) in registers; extremes
-// meet through an xor butterfly inside the wave and LDS across waves; one wave
-// per half then computes each channel's statistics once (lane = channel), and
-// every thread packs its rows.  The packed rows reach the cache before the
-// caller's barrier, so the attention reads them back like older blocks.
-// scratch: (NW + 2) * 2 * 64 floats of LDS.
+// quantize kernel).  Lane l of a wave holds chunk c = l / 8 (channels 8 c ..
+// 8 c + 7) of rows rg, rg + RG, .. (at most 8) with rg = 8 w + l % 8 for the
+// half's wave w, so the 8 lanes sharing a chunk are neighbours:
+//   - per thread: v_min3 / v_max3 over row pairs (for the odd bf16 channel of
+//     a word the raw word is the ordering key, masked afterwards);
+//   - across the 8 lanes of a chunk: three DPP steps (xor 1, xor 2 inside a
+//     quad, then the mirror of the half-row);
+//   - across the half's waves: LDS; one wave per half then computes every
+//     channel's statistics once (lane = channel);
+//   - codes: every thread packs its rows into an LDS copy of the block's rows
+//     (with the destination's 16-byte misalignment), which the half writes to
+//     the cache with 128-bit stores plus byte-exact head and tail.
+// The packed rows reach the cache before the caller's barrier, so the attention
+// reads them back like older blocks.
+// scratch: (NW + 2) * 2 * 64 floats; stage_k, stage_v: 16 + 32 * NW * R bytes each.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 template <int D, int BITS, int NW, bool CHECK>
 __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, int h, int tid,
-                                                  _Float16* st_lds, float* scratch, int& vover) {
+                                                  _Float16* st_lds, float* scratch,
+                                                  uint8_t* stage_k, uint8_t* stage_v, int& vover) {
   static_assert(D == kWave && NW >= 2, "64-channel heads, at least one wave per tensor");
   constexpr int CPR = D / 8;
   constexpr int GT = NW * kWave / 2;  // threads per tensor
-  constexpr int RG = GT / CPR;        // row groups
+  constexpr int WT = NW / 2;          // waves per tensor
+  constexpr int RG = GT / CPR;        // row groups, 8 per wave
   constexpr int MAXR = 8;             // rows per thread (n <= RG * MAXR)
   constexpr float LEVELS = (float)((1 << BITS) - 1);
   const FuseParams& f = p.fz;
   const int n = p.n;
-  const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int tensor = tid / GT;
   const int u = tid % GT;
-  const int c = u % CPR;
-  const int rg = u / CPR;
+  const int wt = u / kWave;
+  const int c = lane >> 3;
+  const int rg = wt * 8 + (lane & 7);
   const int64_t row_stride = (int64_t)p.H * D;
   const int64_t base = ((int64_t)b * n * p.H + h) * D + 8 * c;
   const uint16_t* src = static_cast<const uint16_t*>(f.src[tensor]);
@@ -183,9 +198,14 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     const int r = rg + RG * i;
     if (r < n) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + base + r * row_stride));
   }
+  // exact value of channel j, and the key that orders it
   auto chan = [&](const u32x4& v, int j) {
     const uint32_t x = v[j >> 1];
     return __uint_as_float((j & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  };
+  auto key = [&](const u32x4& v, int j) {
+    const uint32_t x = v[j >> 1];
+    return __uint_as_float((j & 1) ? x : (x << 16));
   };
   float mn[8], mx[8];
 #pragma unroll
@@ -195,44 +215,59 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
   }
   int bad = 0;
 #pragma unroll
-  for (int i = 0; i < MAXR; ++i) {
+  for (int i = 0; i < MAXR; i += 2) {
     if (rg + RG * i < n) {
+      const int i2 = (rg + RG * (i + 1) < n) ? i + 1 : i;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = chan(w[i], j);
-        mn[j] = fminf(mn[j], x);
-        mx[j] = fmaxf(mx[j], x);
-        if constexpr (CHECK) bad |= !__builtin_isfinite(x);
+        const float a = key(w[i], j), e = key(w[i2], j);
+        mn[j] = min3f(mn[j], a, e);
+        mx[j] = max3f(mx[j], a, e);
+      }
+      if constexpr (CHECK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // a bf16 is NaN or +-inf when its exponent bits are all set
+          bad |= ((w[i][q] & 0x7F80u) == 0x7F80u) | ((w[i][q] & 0x7F800000u) == 0x7F800000u);
+          bad |= ((w[i2][q] & 0x7F80u) == 0x7F80u) | ((w[i2][q] & 0x7F800000u) == 0x7F800000u);
+        }
       }
     }
   }
+  // the 8 lanes holding chunk c: xor 1 and xor 2 inside each quad, then the
+  // mirror of each half-row (lane i with lane 7 - i)
 #pragma unroll
-  for (int m = CPR; m < kWave; m <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
-      mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
-    }
+  for (int j = 0; j < 8; ++j) {
+    mn[j] = min3f(mn[j], dpp_f32<0xB1>(mn[j]), mn[j]);
+    mx[j] = max3f(mx[j], dpp_f32<0xB1>(mx[j]), mx[j]);
+    mn[j] = min3f(mn[j], dpp_f32<0x4E>(mn[j]), mn[j]);
+    mx[j] = max3f(mx[j], dpp_f32<0x4E>(mx[j]), mx[j]);
+    mn[j] = min3f(mn[j], dpp_f32<0x141>(mn[j]), mn[j]);
+    mx[j] = max3f(mx[j], dpp_f32<0x141>(mx[j]), mx[j]);
   }
-  float* red = scratch;                    // [NW][2][64]: per-wave extremes
-  float* zi = scratch + NW * 2 * kWave;    // [2][2][64]: zero and reciprocal step
-  if (lane < CPR) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      red[(wave * 2 + 0) * kWave + 8 * lane + j] = mn[j];
-      red[(wave * 2 + 1) * kWave + 8 * lane + j] = mx[j];
-    }
+  float* red = scratch;                          // [tensor][wave][min|max][64]
+  float* zi = scratch + 2 * WT * 2 * kWave;      // [tensor][zero|reciprocal][64]
+  if ((lane & 7) == 0) {
+    float* rm = red + ((tensor * WT + wt) * 2 + 0) * kWave + 8 * c;
+    float* rx = red + ((tensor * WT + wt) * 2 + 1) * kWave + 8 * c;
+    *reinterpret_cast<f32x4*>(rm) = f32x4{mn[0], mn[1], mn[2], mn[3]};
+    *reinterpret_cast<f32x4*>(rm + 4) = f32x4{mn[4], mn[5], mn[6], mn[7]};
+    *reinterpret_cast<f32x4*>(rx) = f32x4{mx[0], mx[1], mx[2], mx[3]};
+    *reinterpret_cast<f32x4*>(rx + 4) = f32x4{mx[4], mx[5], mx[6], mx[7]};
   }
   __syncthreads();
   int flags = 0;
   if (u < kWave) {  // first wave of each half: lane = channel
     const int ch = lane;
-    float lo = __uint_as_float(0x7F800000u), hi = __uint_as_float(0xFF800000u);
+    float lo = red[((tensor * WT) * 2 + 0) * kWave + ch];
+    float hi = red[((tensor * WT) * 2 + 1) * kWave + ch];
 #pragma unroll
-    for (int wv = 0; wv < NW / 2; ++wv) {
-      const int ww = tensor * (NW / 2) + wv;
-      lo = fminf(lo, red[(ww * 2 + 0) * kWave + ch]);
-      hi = fmaxf(hi, red[(ww * 2 + 1) * kWave + ch]);
+    for (int wv = 1; wv < WT; ++wv) {
+      lo = min3f(lo, red[((tensor * WT + wv) * 2 + 0) * kWave + ch], lo);
+      hi = max3f(hi, red[((tensor * WT + wv) * 2 + 1) * kWave + ch], hi);
+    }
+    if (ch & 1) {  // the raw-word keys of odd channels
+      lo = __uint_as_float(__float_as_uint(lo) & 0xFFFF0000u);
+      hi = __uint_as_float(__float_as_uint(hi) & 0xFFFF0000u);
     }
     const GroupStats gst = group_stats<CHECK>(lo, hi, LEVELS, flags);
     const int64_t so = (((int64_t)b * p.H + h) * p.NB + f.block) * D + ch;
@@ -252,7 +287,9 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     zf[j] = zi[(tensor * 2 + 0) * kWave + 8 * c + j];
     inv[j] = zi[(tensor * 2 + 1) * kWave + 8 * c + j];
   }
-  uint8_t* rows = f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R + BITS * c;
+  uint8_t* dst = f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R;
+  const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
+  uint8_t* stg = (tensor == 0 ? stage_k : stage_v) + mis;
 #pragma unroll
   for (int i = 0; i < MAXR; ++i) {
     const int r = rg + RG * i;
@@ -261,15 +298,30 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = chan(w[i], j);
       const uint32_t acc = pack_codes8<BITS>(x, zf, inv);
-      uint8_t* dst = rows + (int64_t)r * p.R;
       if constexpr (BITS == 4) {
-        *reinterpret_cast<uint32_t*>(dst) = acc;  // 4-byte aligned: rows are 32 bytes
+        // 32-byte rows: each chunk's 4 bytes straight to the cache (a wave
+        // writes 8 whole rows per store instruction)
+        *reinterpret_cast<uint32_t*>(dst + r * p.R + BITS * c) = acc;
       } else {
-        dst[0] = (uint8_t)acc;
-        dst[1] = (uint8_t)(acc >> 8);
-        dst[2] = (uint8_t)(acc >> 16);
+        uint8_t* sp = stg + r * p.R + BITS * c;
+        sp[0] = (uint8_t)acc;
+        sp[1] = (uint8_t)(acc >> 8);
+        sp[2] = (uint8_t)(acc >> 16);
       }
     }
+  }
+  if constexpr (BITS != 4) {
+    // 24-byte rows, 3 bytes per chunk, possibly 8 bytes off a 16-byte boundary:
+    // the block's n * R bytes go out of LDS as 128-bit stores, byte-exact ends
+    __syncthreads();
+    const int nbytes = n * p.R;
+    const int head = min((16 - mis) & 15, nbytes);
+    const int body = (nbytes - head) >> 4;
+    const int tail = nbytes - head - (body << 4);
+    for (int k = u; k < body; k += GT)
+      *reinterpret_cast<u32x4*>(dst + head + 16 * k) = *reinterpret_cast<const u32x4*>(stg + head + 16 * k);
+    if (u < head) dst[u] = stg[u];
+    if (u < tail) dst[head + 16 * body + u] = stg[head + 16 * body + u];
   }
   if constexpr (CHECK) {
     if (bad) flags |= KVQ_S_NONFINITE;
@@ -309,6 +361,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const int g = lane >> 5;    // lane group: which 8 of each 16 contraction slots
   const int col = lane & 31;  // this lane's query (S^T / O^T column)
   static_assert(SPLIT == 0 || FUSE == 0, "key ranges are for the attention-only launch");
+  // fused prologue: block rows staged in k_lo (K) and v_t (V), extremes in k_hi
+  static_assert(FUSE == 0 || (sizeof(k_lo) >= 16 + NW * 32 * BITS * D / 8 &&
+                              sizeof(v_t) >= 16 + NW * 32 * BITS * D / 8 &&
+                              sizeof(k_hi) >= (NW + 2) * 2 * kWave * sizeof(float)),
+                "LDS too small for the quantize prologue");
   const int wg = SPLIT ? (int)(blockIdx.x / p.splits) : (int)blockIdx.x;
   const int sp = SPLIT ? (int)blockIdx.x - wg * p.splits : 0;
   const int bh = wg / p.q_tiles;
@@ -332,7 +389,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   int vover = 0;  // a V group's top grid level leaves the binary16 range
   if constexpr (FUSE != 0) {
     quantize_block_wg<D, BITS, NW, FUSE == 2>(p, b, h, tid, st,
-                                              reinterpret_cast<float*>(&k_hi[0][0][0]), vover);
+                                              reinterpret_cast<float*>(&k_hi[0][0][0]),
+                                              reinterpret_cast<uint8_t*>(&k_lo[0][0][0]),
+                                              reinterpret_cast<uint8_t*>(&v_t[0][0][0]), vover);
   }
 
   // ---- item slots: (tensor, key, chunk), fixed for every tile ----------------

@@ -432,4 +432,11 @@ int kvq_stream_copy(const void* src, void* dst, uint64_t n_bytes, hipStream_t st
   return device_status(launch_stream_copy(src, dst, n_bytes, stream));
 }
 
+int kvq_stream_read(const void* src, uint64_t n_bytes, uint32_t* sink, hipStream_t stream) {
+  if (n_bytes % 16 != 0) return KVQ_E_INVAL;
+  if (n_bytes == 0) return KVQ_OK;
+  if (!src || !sink || !aligned16(src)) return KVQ_E_INVAL;
+  return device_status(launch_stream_read(src, n_bytes, sink, stream));
+}
+
 }  // extern "C"

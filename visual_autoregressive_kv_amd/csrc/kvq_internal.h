@@ -236,5 +236,6 @@ hipError_t launch_attend_split(const AttendParams& p, int head_dim, int bits, hi
 hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,
                                   int bits, bool f32src, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n, hipStream_t s);
+hipError_t launch_stream_read(const void* src, uint64_t n, uint32_t* sink, hipStream_t s);
 
 }  // namespace kvq

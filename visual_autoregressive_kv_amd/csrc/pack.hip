@@ -125,6 +125,23 @@ __global__ __launch_bounds__(kWG) void stream_copy_kernel(const u32x4* __restric
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Read-only stream: every 16-byte chunk is loaded once (4 per thread in
+// flight, non-persistent grid); the loaded words are folded with xor and only
+// a result equal to a fixed pattern (never in practice) is stored, so the
+// loads cannot be dropped and almost nothing is written.
+__global__ __launch_bounds__(kWG) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                         uint32_t* __restrict__ sink, uint64_t n16) {
+  const uint64_t i0 = (uint64_t)blockIdx.x * kWG * 4 + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t i = i0 + (uint64_t)k * kWG;
+    if (i < n16) acc ^= __builtin_nontemporal_load(src + i);
+  }
+  const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (x == 0x9E3779B9u) sink[0] = x;
+}
+
 }  // namespace
 
 // Word-aligned stream (pack_mode 1): word w holds codes w*cpw .. w*cpw + cpw - 1
@@ -209,6 +226,16 @@ hipError_t launch_stream_copy(const void* src, void* dst, uint64_t n, hipStream_
   const unsigned grid = 256 * 16;  // 16 workgroups per CU
   hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(kWG), 0, s,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* src, uint64_t n, uint32_t* sink, hipStream_t s) {
+  const uint64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  const uint64_t groups = (n16 + 4 * kWG - 1) / (4 * kWG);
+  if (!dispatch_fits((int64_t)groups, kWG)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)groups), dim3(kWG), 0, s,
+                     static_cast<const u32x4*>(src), sink, n16);
   return hipGetLastError();
 }
 

@@ -99,6 +99,8 @@ def lib() -> C.CDLL:
         L.kvq_attend_split_workspace.argtypes = [C.POINTER(Layout), i32, i32, C.POINTER(u64)]
         L.kvq_stream_copy.restype = C.c_int
         L.kvq_stream_copy.argtypes = [vp, vp, u64, vp]
+        L.kvq_stream_read.restype = C.c_int
+        L.kvq_stream_read.argtypes = [vp, u64, vp, vp]
         _lib = L
     return _lib
 
@@ -325,6 +327,12 @@ def kvq_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst smaller than src")
     _check("kvq_stream_copy", lib().kvq_stream_copy(_dev(src, "src"), _dev(dst, "dst"), n,
+                                                    _stream(stream)))
+
+
+def kvq_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    _check("kvq_stream_read", lib().kvq_stream_read(_dev(src, "src"), n, _dev(sink, "sink"),
                                                     _stream(stream)))
 
 
