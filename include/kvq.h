@@ -81,7 +81,7 @@ extern "C" {
  *   batch       sequences B (>= 1)
  *   heads       H (>= 1)
  *   head_dim    D (multiple of 8; the GPU kernels are built for 64 and 128)
- *   bits        code width: 3 or 4 on the GPU (the byte accounting takes 1..8)
+ *   bits        code width: 2, 3, 4 or 8 on the GPU (the byte accounting takes 1..8)
  *   n_blocks    NB, number of decode blocks (1..KVQ_MAX_BLOCKS)
  *   pack_mode   0 = dense rows: each (b, h, token) row of D codes LSB-first in
  *               ceil(bits*D/8) bytes (the decode path's layout);

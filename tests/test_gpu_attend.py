@@ -89,7 +89,7 @@ def test_video_frames_sampled(oracle):
     check_rows(g, ref, picks, "video frame 3")
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_ragged_edges(oracle, bits, head_dim):
     """Query counts off the 32-row tile (1, 7, 33, 257 -> two workgroups per head),

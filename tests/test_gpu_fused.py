@@ -45,8 +45,13 @@ def decode_both_ways(oracle, wl, layer=0, scale=0.0):
     # 23 blocks: the one-wave fused kernel while the statistics fit its LDS (8
     # blocks), then two launches for short blocks, the workgroup kernel for 40
     vi.Workload("many_blocks", 1, 2, 3, 64, 3, (1,) * 20 + (5, 40, 3), "bf16", seed=29),
+    # the INT2 and INT8 widths (the results table's Infinity rows) through every
+    # fused kernel shape, and INT8 from fp32 on short blocks
+    vi.Workload("int2", 1, 2, 3, 64, 2, vi.VAR_BLOCKS, "bf16", seed=41),
+    vi.Workload("int8_rope", 1, 2, 3, 64, 8, (1, 7, 32, 33, 100, 256), "bf16", rope=True, seed=43),
+    vi.Workload("int8_f32", 1, 2, 3, 64, 8, (1, 4, 9, 16, 25), "f32", seed=47),
 ], ids=["tiny_f32", "d20_int4", "d20_int3_rope", "d24_int4", "edge_int3", "edge_d128",
-        "many_blocks"])
+        "many_blocks", "int2", "int8_rope", "int8_f32"])
 def test_fused_matches_two_calls_and_oracle(oracle, wl):
     kf, vf, ks, vs, ko, vo, steps = decode_both_ways(oracle, wl)
     assert_cache_equal(kf, ko, "fused K")

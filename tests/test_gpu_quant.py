@@ -52,7 +52,7 @@ def test_video_frames_two_pass_path(oracle):
     assert_cache_equal(vg, vo, "V")
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_large_blocks_many_tiles(oracle, bits):
     """Blocks too large for registers with at least 1024 (tensor, b, h) tiles:
     one workgroup per tile streams it twice."""
@@ -62,7 +62,7 @@ def test_large_blocks_many_tiles(oracle, bits):
     assert_cache_equal(vg, vo, "V")
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_ragged_edge_shapes(oracle, bits, src, head_dim):

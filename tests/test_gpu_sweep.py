@@ -1,6 +1,6 @@
 """Seeded sweep over random decode layouts, through every dispatch path of the
 library (one-wave, 2/4/8-wave and fused kernels, two-launch fallbacks,
-head_dim 64 and 128, INT3 and INT4, bf16 and fp32 input, up to 40 blocks, key
+head_dim 64 and 128, INT2, INT3, INT4 and INT8, bf16 and fp32 input, up to 40 blocks, key
 ranges).  Per case, block by block:
   * kvq_quantize_attend's output is bit-identical to kvq_quantize_block then
     kvq_attend_packed, and both caches are bit-exact against the oracle's;
@@ -23,7 +23,7 @@ N_CASES = 48
 def random_workload(i: int) -> vi.Workload:
     rng = np.random.default_rng(1000 + i)
     head_dim = int(rng.choice([64, 128]))
-    bits = int(rng.choice([3, 4]))
+    bits = int(rng.choice([2, 3, 4, 8]))
     src = "f32" if rng.random() < 0.25 else "bf16"
     n_blocks = int(rng.integers(1, 41))
     kind = rng.random()

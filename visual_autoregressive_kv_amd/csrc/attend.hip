@@ -131,6 +131,36 @@ __device__ __forceinline__ void codes_f32(uint32_t w, float c[8]) {
   }
 }
 
+// 3- and 8-bit chunks need two dwords of a row, 2- and 4-bit chunks one
+template <int BITS>
+constexpr bool kTwoWords = BITS == 3 || BITS == 8;
+
+// the 8 codes of one packed chunk as fp32: its bits start at bit `shift` of
+// w0 and continue into w1 (3-bit codes; 8-bit codes 4-7 are all of w1)
+template <int BITS>
+__device__ __forceinline__ void chunk_f32(uint32_t w0, uint32_t w1, int shift, float c[8]) {
+  static_assert(kWidthBuilt<BITS>, "code width not built");
+  if constexpr (BITS == 4) {
+    codes_f32<4>(w0, c);
+  } else if constexpr (BITS == 8) {
+    c[0] = ubyte_f32<0>(w0);
+    c[1] = ubyte_f32<1>(w0);
+    c[2] = ubyte_f32<2>(w0);
+    c[3] = ubyte_f32<3>(w0);
+    c[4] = ubyte_f32<0>(w1);
+    c[5] = ubyte_f32<1>(w1);
+    c[6] = ubyte_f32<2>(w1);
+    c[7] = ubyte_f32<3>(w1);
+  } else if constexpr (BITS == 2) {
+    const uint32_t w = w0 >> shift;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = (float)((w >> (2 * j)) & 3u);
+  } else {
+    const uint64_t v = (uint64_t)w0 | ((uint64_t)w1 << 32);
+    codes_f32<BITS>((uint32_t)(v >> shift), c);
+  }
+}
+
 // Raw buffer view of key tile j of one (b, h)'s packed prefix.  The hardware
 // range check covers the per-lane offset only (not the scalar offset), so the
 // tile's start goes into the base address and the record count is what is
@@ -297,20 +327,17 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = chan(w[i], j);
-      const uint32_t acc = pack_codes8<BITS>(x, zf, inv);
-      if constexpr (BITS == 4) {
-        // 32-byte rows: each chunk's 4 bytes straight to the cache (a wave
+      const Packed8 pk = pack_chunk<BITS>(x, zf, inv);
+      if constexpr (BITS != 3) {
+        // chunks on BITS-byte boundaries go straight to the cache (a wave
         // writes 8 whole rows per store instruction)
-        *reinterpret_cast<uint32_t*>(dst + r * p.R + BITS * c) = acc;
+        store_chunk<BITS>(dst + r * p.R + BITS * c, pk);
       } else {
-        uint8_t* sp = stg + r * p.R + BITS * c;
-        sp[0] = (uint8_t)acc;
-        sp[1] = (uint8_t)(acc >> 8);
-        sp[2] = (uint8_t)(acc >> 16);
+        store_chunk<BITS>(stg + r * p.R + BITS * c, pk);
       }
     }
   }
-  if constexpr (BITS != 4) {
+  if constexpr (BITS == 3) {
     // 24-byte rows, 3 bytes per chunk, possibly 8 bytes off a 16-byte boundary:
     // the block's n * R bytes go out of LDS as 128-bit stores, byte-exact ends
     __syncthreads();
@@ -362,8 +389,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const int col = lane & 31;  // this lane's query (S^T / O^T column)
   static_assert(SPLIT == 0 || FUSE == 0, "key ranges are for the attention-only launch");
   // fused prologue: block rows staged in k_lo (K) and v_t (V), extremes in k_hi
-  static_assert(FUSE == 0 || (sizeof(k_lo) >= 16 + NW * 32 * BITS * D / 8 &&
-                              sizeof(v_t) >= 16 + NW * 32 * BITS * D / 8 &&
+  static_assert(FUSE == 0 || ((BITS != 3 || (sizeof(k_lo) >= 16 + NW * 32 * BITS * D / 8 &&
+                                             sizeof(v_t) >= 16 + NW * 32 * BITS * D / 8)) &&
                               sizeof(k_hi) >= (NW + 2) * 2 * kWave * sizeof(float)),
                 "LDS too small for the quantize prologue");
   const int wg = SPLIT ? (int)(blockIdx.x / p.splits) : (int)blockIdx.x;
@@ -428,8 +455,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     for (int i = 0; i < MAXI; ++i) {
       const __amdgpu_buffer_rsrc_t r = s_tensor[i] == 0 ? rk : rv;
       pre[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i], 0, 0);
-      if constexpr (BITS != 4)
+      if constexpr (kTwoWords<BITS>)
         pre2[i] = __builtin_amdgcn_raw_buffer_load_b32(r, s_voff[i] + 4, 0, 0);
+      else
+        pre2[i] = 0u;
     }
   };
   if (early0) issue_loads(j_begin, preA, pre2A);
@@ -500,17 +529,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         } while (t >= s_next[i]);
         load_stats(s_blk[i], s_tensor[i], cg, s_z[i], s_s[i]);
       }
-      uint32_t w;
-      if constexpr (BITS == 4) {
-        w = pre[i];
-      } else {
-        const uint64_t v = (uint64_t)pre[i] | ((uint64_t)pre2[i] << 32);
-        w = (uint32_t)(v >> s_shift[i]);
-      }
       // keys past the prefix read codes 0 (buffer range check) and keep the
       // last block's statistics: finite values whose scores are masked out
       float cf[8], x[8];
-      codes_f32<BITS>(w, cf);
+      chunk_f32<BITS>(pre[i], pre2[i], s_shift[i], cf);
 #pragma unroll
       for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]);
       if (s_tensor[i] != 0 && vhalf) {
@@ -717,7 +739,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
 // The statistics and packed rows also go to LDS for the attention that
 // follows in the same launch; the cache writes serve later blocks.
 // ---------------------------------------------------------------------------
-constexpr int kFusedRowBytes = 32;  // LDS bytes per packed row of the fused block (R <= 32)
+// LDS bytes per packed row of the fused block: R = 8 * BITS at head_dim 64,
+// plus the 4 bytes a two-dword chunk read may touch past the row
+template <int BITS>
+constexpr int kFusedRowBytes = BITS == 8 ? 64 : 32;
 
 template <int D, int BITS, bool F32, bool CHECK>
 __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b, int h, int lane,
@@ -773,7 +798,7 @@ __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b
       inv[j] = scratch[D + 8 * cg + j];
     }
     uint8_t* rows = f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R;
-    uint8_t* lrows = rows_lds + tensor * KT * kFusedRowBytes;
+    uint8_t* lrows = rows_lds + tensor * KT * kFusedRowBytes<BITS>;
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
       const int t = tl + TL * i;
@@ -796,17 +821,9 @@ __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b
             x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
           }
         }
-        const uint32_t acc = pack_codes8<BITS>(x, zf, inv);
-        uint8_t* dst = rows + (int64_t)t * p.R + BITS * cg;
-        uint8_t* ldst = lrows + t * p.R + BITS * cg;
-        if constexpr (BITS == 4) {
-          *reinterpret_cast<uint32_t*>(dst) = acc;  // 4-byte aligned: rows are 32 bytes
-          *reinterpret_cast<uint32_t*>(ldst) = acc;
-        } else {
-          dst[0] = ldst[0] = (uint8_t)acc;
-          dst[1] = ldst[1] = (uint8_t)(acc >> 8);
-          dst[2] = ldst[2] = (uint8_t)(acc >> 16);
-        }
+        const Packed8 pk = pack_chunk<BITS>(x, zf, inv);
+        store_chunk<BITS>(rows + (int64_t)t * p.R + BITS * cg, pk);
+        store_chunk<BITS>(lrows + t * p.R + BITS * cg, pk);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // scratch reuse
@@ -844,7 +861,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   __shared__ __align__(16) _Float16 st_all[kSmallWaves][kSmallStatsHalves];
   __shared__ int bend_all[kSmallWaves][KVQ_MAX_BLOCKS];
   // fused launch: the packed rows of block k (K then V) for the attention below
-  __shared__ __align__(16) uint8_t rows_all[kSmallWaves][FUSE != 0 ? 2 * KT * kFusedRowBytes : 16];
+  __shared__ __align__(16) uint8_t rows_all[kSmallWaves][FUSE != 0 ? 2 * KT * kFusedRowBytes<BITS> : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -891,14 +908,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kpre[ks][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, k_voff[ks], 0, 0);
-      if constexpr (BITS != 4)
-        kpre[ks][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, k_voff[ks] + 4, 0, 0);
+      kpre[ks][1] = kTwoWords<BITS> ? __builtin_amdgcn_raw_buffer_load_b32(rk, k_voff[ks] + 4, 0, 0) : 0u;
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       vpre[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_voff[i], 0, 0);
-      if constexpr (BITS != 4)
-        vpre[i][1] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_voff[i] + 4, 0, 0);
+      vpre[i][1] = kTwoWords<BITS> ? __builtin_amdgcn_raw_buffer_load_b32(rv, v_voff[i] + 4, 0, 0) : 0u;
     }
   };
   issue_loads(0);
@@ -953,11 +968,6 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
     z = *reinterpret_cast<const f16x8*>(zr);
     s = *reinterpret_cast<const f16x8*>(zr + D);
   };
-  auto bits_of = [&](const uint32_t* w, int shift) -> uint32_t {
-    if constexpr (BITS == 4) return w[0];
-    const uint64_t v = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-    return (uint32_t)(v >> shift);
-  };
 
   f32x16 o[QT][MT];
   float m_run[QT], negmc[QT], l_run[QT];
@@ -979,12 +989,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kc[ks][0] = kpre[ks][0];
-      kc[ks][1] = BITS != 4 ? kpre[ks][1] : 0u;
+      kc[ks][1] = kpre[ks][1];
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       vc[i][0] = vpre[i][0];
-      vc[i][1] = BITS != 4 ? vpre[i][1] : 0u;
+      vc[i][1] = vpre[i][1];
     }
     if (j + 1 < n_tiles) issue_loads(j + 1);
     // this lane's key; past the prefix its codes read 0 and dequantize to
@@ -995,18 +1005,18 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
       const int r = tk - (int)p.fz.off;  // row within block k
       if (r >= 0 && live) {
         const uint8_t* kr = qrows + r * p.R;
-        const uint8_t* vr = qrows + KT * kFusedRowBytes + r * p.R;
+        const uint8_t* vr = qrows + KT * kFusedRowBytes<BITS> + r * p.R;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int bo = k_voff[ks] - col * p.R;  // byte offset within the row
           kc[ks][0] = *reinterpret_cast<const uint32_t*>(kr + bo);
-          if constexpr (BITS != 4) kc[ks][1] = *reinterpret_cast<const uint32_t*>(kr + bo + 4);
+          if constexpr (kTwoWords<BITS>) kc[ks][1] = *reinterpret_cast<const uint32_t*>(kr + bo + 4);
         }
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
           const int bo = v_voff[i] - col * p.R;
           vc[i][0] = *reinterpret_cast<const uint32_t*>(vr + bo);
-          if constexpr (BITS != 4) vc[i][1] = *reinterpret_cast<const uint32_t*>(vr + bo + 4);
+          if constexpr (kTwoWords<BITS>) vc[i][1] = *reinterpret_cast<const uint32_t*>(vr + bo + 4);
         }
       }
     }
@@ -1023,7 +1033,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
       f16x8 z, sc;
       stats(1, v_cg[i], z, sc);
       float cf[8], x[8];
-      codes_f32<BITS>(bits_of(vc[i], v_shift[i]), cf);
+      chunk_f32<BITS>(vc[i][0], vc[i][1], v_shift[i], cf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
       if (vhalf) {
@@ -1056,7 +1066,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
         f16x8 z, sc;
         stats(0, 2 * ks + g, z, sc);
         float cf[8], x[8];
-        codes_f32<BITS>(bits_of(kc[ks], k_shift[ks]), cf);
+        chunk_f32<BITS>(kc[ks][0], kc[ks][1], k_shift[ks], cf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
         u32x4 hi, lo;
@@ -1196,9 +1206,24 @@ hipError_t launch_t(const AttendParams& p, hipStream_t s) {
 
 }  // namespace
 
+// head_dim x code width dispatch of a launcher template L<D, BITS>
+#define KVQ_DISPATCH(L, head_dim, bits, ...)            \
+  do {                                                  \
+    switch ((head_dim) * 16 + (bits)) {                 \
+      case 64 * 16 + 2: return L<64, 2>(__VA_ARGS__);   \
+      case 64 * 16 + 3: return L<64, 3>(__VA_ARGS__);   \
+      case 64 * 16 + 4: return L<64, 4>(__VA_ARGS__);   \
+      case 64 * 16 + 8: return L<64, 8>(__VA_ARGS__);   \
+      case 128 * 16 + 2: return L<128, 2>(__VA_ARGS__); \
+      case 128 * 16 + 3: return L<128, 3>(__VA_ARGS__); \
+      case 128 * 16 + 4: return L<128, 4>(__VA_ARGS__); \
+      case 128 * 16 + 8: return L<128, 8>(__VA_ARGS__); \
+      default: return hipErrorInvalidValue;             \
+    }                                                   \
+  } while (0)
+
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
-  if (head_dim == 64) return bits == 4 ? launch_t<64, 4>(p, s) : launch_t<64, 3>(p, s);
-  return bits == 4 ? launch_t<128, 4>(p, s) : launch_t<128, 3>(p, s);
+  KVQ_DISPATCH(launch_t, head_dim, bits, p, s);
 }
 
 namespace {
@@ -1242,8 +1267,7 @@ hipError_t launch_split_t(const AttendParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attend_split(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
-  if (head_dim == 64) return bits == 4 ? launch_split_t<64, 4>(p, s) : launch_split_t<64, 3>(p, s);
-  return bits == 4 ? launch_split_t<128, 4>(p, s) : launch_split_t<128, 3>(p, s);
+  KVQ_DISPATCH(launch_split_t, head_dim, bits, p, s);
 }
 
 namespace {
@@ -1280,8 +1304,13 @@ hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, i
     AttendParams p = a;
     fill_fuse(p, q);
     const bool check = q.status != nullptr;
-    return bits == 4 ? launch_small_fused<4>(p, f32src, check, s)
-                     : launch_small_fused<3>(p, f32src, check, s);
+    switch (bits) {
+      case 2: return launch_small_fused<2>(p, f32src, check, s);
+      case 3: return launch_small_fused<3>(p, f32src, check, s);
+      case 4: return launch_small_fused<4>(p, f32src, check, s);
+      case 8: return launch_small_fused<8>(p, f32src, check, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   // larger blocks: the workgroup kernels with one query tile per (sequence, head)
   const int waves = (a.n + 31) / 32;
@@ -1289,8 +1318,13 @@ hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, i
     AttendParams p = a;
     fill_fuse(p, q);
     const bool check = q.status != nullptr;
-    if (bits == 4) return launch_wg_fused<4>(p, waves, check, s);
-    return launch_wg_fused<3>(p, waves, check, s);
+    switch (bits) {
+      case 2: return launch_wg_fused<2>(p, waves, check, s);
+      case 3: return launch_wg_fused<3>(p, waves, check, s);
+      case 4: return launch_wg_fused<4>(p, waves, check, s);
+      case 8: return launch_wg_fused<8>(p, waves, check, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   const hipError_t e = launch_quantize(q, head_dim, bits, f32src, s);
   if (e != hipSuccess) return e;

@@ -38,10 +38,10 @@ int validate_layout(const kvq_layout* L) {
   return KVQ_OK;
 }
 
-// kernels are built for 3/4-bit codes and head_dim 64/128
+// kernels are built for 2/3/4/8-bit codes and head_dim 64/128
 int gpu_supported(const kvq_layout* L) {
   if (L->pack_mode != 0) return KVQ_E_UNSUPPORTED;  // the decode path keeps dense rows
-  if (L->bits != 3 && L->bits != 4) return KVQ_E_UNSUPPORTED;
+  if (L->bits != 2 && L->bits != 3 && L->bits != 4 && L->bits != 8) return KVQ_E_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return KVQ_E_UNSUPPORTED;
   // one (b, h)'s rows are addressed with 32-bit buffer offsets
   int64_t T = 0;

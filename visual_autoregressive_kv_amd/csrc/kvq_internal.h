@@ -127,6 +127,56 @@ __device__ __forceinline__ uint32_t pack_codes8(const float x[8], const float zf
   return acc - PackMagic<BITS>::value();
 }
 
+// Code widths the GPU kernels are built for.  Rows of D codes take 8 * BITS
+// bytes per 8-code chunk (BITS bytes); chunks of 2-, 4- and 8-bit codes sit on
+// BITS-byte boundaries, 3-bit chunks straddle them.
+template <int BITS>
+constexpr bool kWidthBuilt = BITS == 2 || BITS == 3 || BITS == 4 || BITS == 8;
+
+// Packed bits of one chunk of 8 codes, LSB-first: all of them in lo for up to 4
+// bits per code; codes 0-3 in lo and 4-7 in hi for 8 bits.
+struct Packed8 {
+  uint32_t lo, hi;
+};
+
+template <int BITS>
+__device__ __forceinline__ Packed8 pack_chunk(const float x[8], const float zf[8],
+                                              const float inv[8]) {
+  static_assert(kWidthBuilt<BITS>, "code width not built");
+  if constexpr (BITS <= 4) {
+    return Packed8{pack_codes8<BITS>(x, zf, inv), 0u};
+  } else {
+    constexpr float LEVELS = (float)((1 << BITS) - 1);
+    uint32_t acc[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = (x[j] - zf[j]) * inv[j];
+      const float f = __builtin_amdgcn_fmed3f(u, 0.0f, LEVELS) + 8388608.0f;  // 2^23: rne
+      acc[j >> 2] += __float_as_uint(f) << (8 * (j & 3));
+    }
+    // of the four 0x4B000000 exponent words per half only the unshifted one
+    // survives modulo 2^32
+    return Packed8{acc[0] - 0x4B000000u, acc[1] - 0x4B000000u};
+  }
+}
+
+// store one packed chunk: BITS bytes at dst (aligned to BITS bytes for 2, 4
+// and 8 bits; byte stores for 3)
+template <int BITS>
+__device__ __forceinline__ void store_chunk(uint8_t* dst, const Packed8& v) {
+  if constexpr (BITS == 2) {
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v.lo;
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint32_t*>(dst) = v.lo;
+  } else if constexpr (BITS == 8) {
+    *reinterpret_cast<uint2*>(dst) = uint2{v.lo, v.hi};
+  } else {
+    dst[0] = (uint8_t)v.lo;
+    dst[1] = (uint8_t)(v.lo >> 8);
+    dst[2] = (uint8_t)(v.lo >> 16);
+  }
+}
+
 struct QuantParams {
   const void* src[2];  // K, V: [B][n][H][D]
   uint8_t* codes[2];   // [B][H][T][R]

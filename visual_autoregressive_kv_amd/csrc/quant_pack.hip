@@ -33,7 +33,10 @@ namespace {
 
 constexpr int kWG = 256;
 constexpr int kMaxRpt = 8;
-constexpr int kStageBytes = kWG * kMaxRpt * 4 + 16 * 32;
+// LDS staging of one pass of packed rows: up to kWG * kMaxRpt chunks of BITS
+// bytes, plus room for every tile slot's 16-byte misalignment
+template <int BITS>
+constexpr int kStageBytes = kWG * kMaxRpt * (BITS > 4 ? BITS : 4) + 16 * 32;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -134,16 +137,8 @@ __device__ __forceinline__ void pack_store(const Chunk<F32> (&v)[kMaxRpt], int n
       float xv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) xv[j] = chan<F32>(v[i], j);
-      const uint32_t acc = pack_codes8<BITS>(xv, zf, inv);
       const int chunk = (r0 + i * rps) * CPR + cg;  // within this pass
-      uint8_t* sp = my_stage + mis + chunk * BITS;
-      if constexpr (BITS == 4) {
-        *reinterpret_cast<uint32_t*>(sp) = acc;
-      } else {
-        sp[0] = (uint8_t)acc;
-        sp[1] = (uint8_t)(acc >> 8);
-        sp[2] = (uint8_t)(acc >> 16);
-      }
+      store_chunk<BITS>(my_stage + mis + chunk * BITS, pack_chunk<BITS>(xv, zf, inv));
     }
   }
   __syncthreads();
@@ -162,7 +157,7 @@ template <int D, int BITS, bool F32, bool CHECK, bool STREAM>
 __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
   constexpr int CPR = D / 8;  // 8-channel chunks per row
   constexpr float LEVELS = (float)((1 << BITS) - 1);
-  __shared__ __align__(16) uint8_t stage[kStageBytes];
+  __shared__ __align__(16) uint8_t stage[kStageBytes<BITS>];
   __shared__ float red_mn[kWG / kWave][CPR][8];
   __shared__ float red_mx[kWG / kWave][CPR][8];
 
@@ -420,7 +415,7 @@ __global__ __launch_bounds__(D) void slice_stats_kernel(QuantParams p, int n_sli
 template <int D, int BITS, bool F32>
 __global__ __launch_bounds__(kWG) void slice_pack_kernel(QuantParams p, int n_slices) {
   constexpr int CPR = D / 8;
-  __shared__ __align__(16) uint8_t stage[kStageBytes];
+  __shared__ __align__(16) uint8_t stage[kStageBytes<BITS>];
   const int tid = threadIdx.x;
   const int64_t tile = blockIdx.x / n_slices;
   const int slice = (int)(blockIdx.x - tile * n_slices);
@@ -488,10 +483,20 @@ hipError_t launch_t(const QuantParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int BITS>
+hipError_t launch_b(const QuantParams& p, bool f32src, hipStream_t s) {
+  return f32src ? launch_t<D, BITS, true>(p, s) : launch_t<D, BITS, false>(p, s);
+}
+
 template <int D>
 hipError_t launch_d(const QuantParams& p, int bits, bool f32src, hipStream_t s) {
-  if (bits == 4) return f32src ? launch_t<D, 4, true>(p, s) : launch_t<D, 4, false>(p, s);
-  return f32src ? launch_t<D, 3, true>(p, s) : launch_t<D, 3, false>(p, s);
+  switch (bits) {
+    case 2: return launch_b<D, 2>(p, f32src, s);
+    case 3: return launch_b<D, 3>(p, f32src, s);
+    case 4: return launch_b<D, 4>(p, f32src, s);
+    case 8: return launch_b<D, 8>(p, f32src, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
