@@ -58,6 +58,8 @@ def lib():
         L.kvqr_codes_per_word.argtypes = [C.c_int32]
         L.kvqr_stream_words.restype = C.c_int64
         L.kvqr_stream_words.argtypes = [C.c_int32, C.c_int64]
+        L.kvqr_block_word_offset.restype = C.c_int64
+        L.kvqr_block_word_offset.argtypes = [C.POINTER(Layout), C.c_int32]
         L.kvqr_quantize_group.restype = C.c_int
         L.kvqr_quantize_group.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
                                           C.c_void_p, C.c_void_p, C.c_void_p]
@@ -138,11 +140,18 @@ def quantize_group(x: np.ndarray, bits: int):
     return int(st), int(z[0]), int(s[0]), codes[: x.size]
 
 
+def block_word_offset(L: Layout, block: int) -> int:
+    return int(lib().kvqr_block_word_offset(C.byref(L), block))
+
+
 def alloc_cache(L: Layout) -> Dict[str, np.ndarray]:
     T = int(sum(L.block_tokens[i] for i in range(L.n_blocks)))
-    R = row_bytes(L.bits, L.head_dim)
+    if L.pack_mode == 2:  # [B][H] word streams, one per block, 4 bytes a word
+        codes = np.zeros((L.batch, L.heads, 4 * block_word_offset(L, L.n_blocks)), np.uint8)
+    else:
+        codes = np.zeros((L.batch, L.heads, T, row_bytes(L.bits, L.head_dim)), np.uint8)
     return {
-        "codes": np.zeros((L.batch, L.heads, T, R), np.uint8),
+        "codes": codes,
         "zero": np.zeros((L.batch, L.heads, L.n_blocks, L.head_dim), np.uint16),
         "scale": np.zeros((L.batch, L.heads, L.n_blocks, L.head_dim), np.uint16),
     }

@@ -19,7 +19,11 @@
  *     "VAR-Q Tables 2-4" results page (BF16 16.60 -> INT4 4.64, 72.06%);
  *   - packing: each (sequence, head, token) row of D codes is an LSB-first bit
  *     stream, code d occupying stream bits [b*d, b*d+b); 3-bit codes therefore
- *     straddle byte boundaries;
+ *     straddle byte boundaries (pack_mode 0);
+ *   - block-aligned words (pack_mode 2): each (sequence, head, block) stream of
+ *     n_k x D codes, row after row, in 32-bit words of floor(32/b) codes, every
+ *     block from a fresh word, so INT3 stores ten codes per word and a block is
+ *     written once, when decoding reaches it;
  *   - attention: softmax(scale * q . k_hat) v_hat over the whole prefix of
  *     blocks 0..k, no mask inside block k, in binary64.
  *
@@ -30,10 +34,12 @@
  *   quantize_group  closed forms ({0..15} -> identity grid, constant group,
  *                   {-1, 1}), brute-force argmin over the grid, half-step bound;
  *   pack/unpack     hand-computed worked bytes (tests/golden/pack_examples.txt),
- *                   exhaustive round trips;
+ *                   exhaustive round trips; block-aligned words by a
+ *                   hand-worked two-block example (block_words_example.txt);
  *   attend          independent float64 numpy softmax attention, closed forms
  *                   (single key, identical keys), block causality, permutation;
- *   bytes           the page's KV memory column (tests/golden/kv_table.txt).
+ *   bytes           the page's KV memory column (tests/golden/kv_table.txt),
+ *                   every layout.
  */
 #include "kvq_oracle.h"
 
@@ -152,7 +158,7 @@ int kvqr_validate(const kvqr_layout* L) {
   if (L->head_dim < 8 || L->head_dim % 8 != 0) return KVQR_E_INVAL;
   if (L->bits < 1 || L->bits > 8) return KVQR_E_INVAL;
   if (L->n_blocks < 1 || L->n_blocks > KVQR_MAX_BLOCKS) return KVQR_E_INVAL;
-  if (L->pack_mode != 0 && L->pack_mode != 1) return KVQR_E_INVAL;
+  if (L->pack_mode < 0 || L->pack_mode > 2) return KVQR_E_INVAL;
   for (int i = 0; i < L->n_blocks; i++)
     if (L->block_tokens[i] < 1) return KVQR_E_INVAL;
   return KVQR_OK;
@@ -166,6 +172,18 @@ int64_t kvqr_block_offset(const kvqr_layout* L, int32_t block) {
 
 int64_t kvqr_total_tokens(const kvqr_layout* L, int32_t n_filled) {
   return kvqr_block_offset(L, n_filled);
+}
+
+/* Block-aligned word layout (pack_mode 2): each (b, h) cache is the sequence of
+ * its blocks' streams; block k's stream is its n_k x D codes, row after row,
+ * in 32-bit words of floor(32 / bits) codes (as in pack_mode 1), and starts on
+ * a fresh word, so every block is written once, when the generation loop hands
+ * it over.  Words of blocks 0..block-1 come before block `block`. */
+int64_t kvqr_block_word_offset(const kvqr_layout* L, int32_t block) {
+  int64_t w = 0;
+  for (int32_t k = 0; k < block; k++)
+    w += kvqr_stream_words(L->bits, (int64_t)L->block_tokens[k] * L->head_dim);
+  return w;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -273,6 +291,17 @@ static void unpack_words(int32_t bits, const uint8_t* src, int64_t n, uint8_t* c
     codes[i] = (uint8_t)((word >> (bits * k)) & ((1u << bits) - 1u));
   }
 }
+/* codes i0 .. i0 + n - 1 of a word stream */
+static void unpack_words_at(int32_t bits, const uint8_t* src, int64_t i0, int64_t n,
+                            uint8_t* codes) {
+  const int64_t cpw = kvqr_codes_per_word(bits);
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t w = (i0 + i) / cpw, k = (i0 + i) % cpw;
+    uint32_t word = 0;
+    for (int byte = 0; byte < 4; byte++) word |= (uint32_t)src[4 * w + byte] << (8 * byte);
+    codes[i] = (uint8_t)((word >> (bits * k)) & ((1u << bits) - 1u));
+  }
+}
 
 int kvqr_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,
               int32_t row_len, uint8_t* dst, int64_t dst_row_stride) {
@@ -340,9 +369,15 @@ static int quantize_one(const kvqr_layout* L, int32_t block, int32_t src_dtype, 
         c.scale[sidx] = sb;
         for (int32_t t = 0; t < n; t++) tile[(int64_t)t * D + d] = gcodes[t];
       }
-      for (int32_t t = 0; t < n; t++) {
-        uint8_t* row = c.codes + (((int64_t)b * H + h) * T + off + t) * R;
-        kvqr_pack_row(L->bits, tile + (int64_t)t * D, D, row);
+      if (L->pack_mode == 2) { /* the block's stream of n x D codes, from a fresh word */
+        const int64_t W = kvqr_block_word_offset(L, NB);
+        uint8_t* words = c.codes + (((int64_t)b * H + h) * W + kvqr_block_word_offset(L, block)) * 4;
+        pack_words(L->bits, tile, (int64_t)n * D, words);
+      } else {
+        for (int32_t t = 0; t < n; t++) {
+          uint8_t* row = c.codes + (((int64_t)b * H + h) * T + off + t) * R;
+          kvqr_pack_row(L->bits, tile + (int64_t)t * D, D, row);
+        }
       }
     }
   }
@@ -356,7 +391,7 @@ int kvqr_quantize_block(const kvqr_layout* L, int32_t block, int32_t src_dtype,
                         const void* k_src, const void* v_src, kvqr_cache k_cache,
                         kvqr_cache v_cache) {
   if (kvqr_validate(L) != KVQR_OK) return KVQR_E_INVAL;
-  if (L->pack_mode != 0) return KVQR_E_INVAL; /* the decode path keeps dense rows */
+  if (L->pack_mode == 1) return KVQR_E_INVAL; /* one stream per (b, h): not block-writable */
   if (block < 0 || block >= L->n_blocks) return KVQR_E_INVAL;
   if (src_dtype != KVQR_F32 && src_dtype != KVQR_BF16) return KVQR_E_INVAL;
   if (!k_src || !v_src || !k_cache.codes || !k_cache.zero || !k_cache.scale || !v_cache.codes ||
@@ -391,8 +426,15 @@ static void dequant_bh(const kvqr_layout* L, kvqr_cache c, int32_t b, int32_t h,
   uint8_t* codes = (uint8_t*)malloc((size_t)D);
   for (int64_t t = 0; t < T; t++) {
     int32_t k = block_of_token(L, t);
-    const uint8_t* row = c.codes + (((int64_t)b * H + h) * Tmax + t) * R;
-    kvqr_unpack_row(L->bits, row, D, codes);
+    if (L->pack_mode == 2) { /* row t - off_k of block k's word stream */
+      const int64_t W = kvqr_block_word_offset(L, NB);
+      const uint8_t* words =
+          c.codes + (((int64_t)b * H + h) * W + kvqr_block_word_offset(L, k)) * 4;
+      unpack_words_at(L->bits, words, (t - kvqr_block_offset(L, k)) * D, D, codes);
+    } else {
+      const uint8_t* row = c.codes + (((int64_t)b * H + h) * Tmax + t) * R;
+      kvqr_unpack_row(L->bits, row, D, codes);
+    }
     for (int32_t d = 0; d < D; d++) {
       int64_t sidx = (((int64_t)b * H + h) * NB + k) * D + d;
       float z = kvqr_h2f(c.zero[sidx]);
@@ -404,7 +446,7 @@ static void dequant_bh(const kvqr_layout* L, kvqr_cache c, int32_t b, int32_t h,
 }
 
 int kvqr_dequantize(const kvqr_layout* L, int32_t n_filled, kvqr_cache c, float* out) {
-  if (kvqr_validate(L) != KVQR_OK || L->pack_mode != 0) return KVQR_E_INVAL;
+  if (kvqr_validate(L) != KVQR_OK || L->pack_mode == 1) return KVQR_E_INVAL;
   if (n_filled < 0 || n_filled > L->n_blocks || !out) return KVQR_E_INVAL;
   const int32_t B = L->batch, H = L->heads, D = L->head_dim;
   const int64_t T = kvqr_total_tokens(L, n_filled);
@@ -439,7 +481,7 @@ static void attend_one(int32_t D, int64_t T, const double* q, const float* kh, c
 
 static int attend_args_ok(const kvqr_layout* L, int32_t block, const uint16_t* q, kvqr_cache k,
                           kvqr_cache v) {
-  if (kvqr_validate(L) != KVQR_OK || L->pack_mode != 0) return 0;
+  if (kvqr_validate(L) != KVQR_OK || L->pack_mode == 1) return 0;
   if (block < 0 || block >= L->n_blocks || !q) return 0;
   if (!k.codes || !k.zero || !k.scale || !v.codes || !v.zero || !v.scale) return 0;
   return 1;
@@ -515,6 +557,8 @@ int kvqr_bytes(const kvqr_layout* L, int32_t n_filled, uint64_t* code_bytes,
   uint64_t T = (uint64_t)kvqr_total_tokens(L, n_filled);
   if (L->pack_mode == 1) /* each (b, h) cache is one word-aligned stream of T*D codes */
     *code_bytes = BH * 4u * (uint64_t)kvqr_stream_words(L->bits, (int64_t)T * L->head_dim);
+  else if (L->pack_mode == 2) /* one word-aligned stream per (b, h, block) */
+    *code_bytes = BH * 4u * (uint64_t)kvqr_block_word_offset(L, n_filled);
   else
     *code_bytes = BH * T * (uint64_t)kvqr_row_bytes(L->bits, L->head_dim);
   /* one binary16 zero + one binary16 step per (block, channel) */

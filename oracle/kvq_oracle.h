@@ -53,7 +53,8 @@ typedef struct {
 } kvqr_layout;
 
 typedef struct {
-  uint8_t* codes;   /* [B][H][T][R] packed rows, T = sum of block_tokens */
+  uint8_t* codes;   /* [B][H][T][R] packed rows, T = sum of block_tokens (pack_mode 0);
+                       [B][H][W] 32-bit words, W = words of all blocks (pack_mode 2) */
   uint16_t* zero;   /* [B][H][NB][D] binary16 bit patterns */
   uint16_t* scale;  /* [B][H][NB][D] binary16 bit patterns */
 } kvqr_cache;
@@ -73,6 +74,9 @@ int32_t kvqr_row_bytes(int32_t bits, int32_t head_dim);
 /* word-aligned layout (pack_mode 1): codes per 32-bit word, words of a stream */
 int32_t kvqr_codes_per_word(int32_t bits);
 int64_t kvqr_stream_words(int32_t bits, int64_t n_codes);
+/* block-aligned word layout (pack_mode 2): words before block `block` of one
+ * (b, h) cache; each block's n_k x D codes start on a fresh word */
+int64_t kvqr_block_word_offset(const kvqr_layout* L, int32_t block);
 
 /* one (block, channel) group: n values at x[i*stride] */
 int kvqr_quantize_group(const float* x, int64_t n, int64_t stride, int32_t bits,

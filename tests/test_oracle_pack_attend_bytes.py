@@ -233,7 +233,8 @@ def test_bytes_reproduce_the_pages_int4_and_bf16_rows(oracle):
 def test_bytes_dense_int3_and_the_tables_int3_rows(oracle):
     """Dense 3-bit rows give 78.31% on the VAR schedule; the table's INT3 rows
     (77.06%, 3.81 / 5.48 / 8.57) are reproduced by the word-aligned layout
-    (pack_mode 1, 10 codes per 32-bit word).  The decode path keeps dense rows."""
+    (pack_mode 1, 10 codes per 32-bit word), one stream per (sequence, head)
+    that the decode path cannot write a block at a time."""
     seen = 0
     for m, layers, width, batch, method, prec, kv, saving in read_kv_table():
         if prec != "INT3":
@@ -302,14 +303,102 @@ def test_word_aligned_equals_dense_stream_when_words_fill(oracle, bits):
 
 
 def test_word_aligned_layout_rejected_on_the_decode_path(oracle):
+    """One stream per (b, h) cannot take a block at a time: pack_mode 1 is for
+    size accounting only; pack_mode 3 does not exist."""
     wl = vi.Workload("w", 1, 1, 2, 64, 3, (4, 9), "bf16", seed=3)
     L = oracle.make_layout(1, 2, 64, 3, (4, 9), pack_mode=1)
     c = oracle.alloc_cache(oracle.make_layout(1, 2, 64, 3, (4, 9)))
     assert oracle.quantize_block(L, 0, vi.kv_block(wl, 0, "k", 0), vi.kv_block(wl, 0, "v", 0),
                                  c, c) == oracle.E_INVAL
-    L.pack_mode = 2
+    L.pack_mode = 3
     with pytest.raises(Exception):
         oracle.nbytes(L, 1)
+
+
+def read_block_words_example():
+    blocks, packed = {}, None
+    for line in open(os.path.join(GOLDEN, "block_words_example.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, val = [x.strip() for x in line.split("|")]
+        if key == "packed":
+            packed = bytes.fromhex(val)
+        else:
+            blocks[int(key)] = np.array([[float(v) for v in r.split()] for r in val.split(";")],
+                                        np.float32)
+    return blocks, packed
+
+
+def test_block_words_worked_example(oracle):
+    """Hand-worked bytes of the block-aligned word layout (two INT3 blocks)."""
+    rows, expect = read_block_words_example()
+    sizes = tuple(rows[k].shape[0] for k in sorted(rows))
+    L = oracle.make_layout(1, 1, 8, 3, sizes, pack_mode=2)
+    assert oracle.block_word_offset(L, 1) == 2 and oracle.block_word_offset(L, 2) == 5
+    kc, vc = oracle.alloc_cache(L), oracle.alloc_cache(L)
+    assert kc["codes"].shape == (1, 1, 20)
+    for k in sorted(rows):
+        x = rows[k].reshape(1, -1, 1, 8)  # [b][t][h][d]
+        assert oracle.quantize_block(L, k, x, 7.0 - x, kc, vc) == oracle.OK
+        assert (oracle.h2f(kc["zero"][0, 0, k]) == 0).all()
+        assert (oracle.h2f(kc["scale"][0, 0, k]) == 1).all()
+    assert kc["codes"].tobytes() == expect
+    # V = 7 - K: every code complemented, padding bits still zero
+    vwords = vc["codes"].view("<u4").ravel()
+    kwords = kc["codes"].view("<u4").ravel()
+    live = [(1 << 30) - 1, (1 << 18) - 1, (1 << 30) - 1, (1 << 30) - 1, (1 << 12) - 1]
+    assert [int(v) for v in vwords] == [int(k) ^ m for k, m in zip(kwords, live)]
+    assert oracle.nbytes(L, 1)[0] == 8 and oracle.nbytes(L, 2)[0] == 20
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_block_words_decode_equal_to_dense_rows(oracle, bits):
+    """The layout changes where codes sit, not what they are: dequantized
+    caches and attention outputs are identical to dense rows, on ragged blocks
+    whose streams end mid-word."""
+    blocks = (1, 3, 7, 12)
+    wl = vi.Workload("w", 1, 2, 3, 24, bits, blocks, "bf16", seed=40 + bits)
+    L0 = oracle.make_layout(2, 3, 24, bits, blocks)
+    L2 = oracle.make_layout(2, 3, 24, bits, blocks, pack_mode=2)
+    c0 = [oracle.alloc_cache(L0), oracle.alloc_cache(L0)]
+    c2 = [oracle.alloc_cache(L2), oracle.alloc_cache(L2)]
+    for k in range(len(blocks)):
+        ks, vs = vi.kv_block(wl, 0, "k", k), vi.kv_block(wl, 0, "v", k)
+        assert oracle.quantize_block(L0, k, ks, vs, *c0) == oracle.OK
+        assert oracle.quantize_block(L2, k, ks, vs, *c2) == oracle.OK
+        n = k + 1
+        for a, b in zip(c0, c2):
+            assert np.array_equal(a["zero"], b["zero"]) and np.array_equal(a["scale"], b["scale"])
+            assert np.array_equal(oracle.dequantize(L0, n, a), oracle.dequantize(L2, n, b))
+        q = vi.q_block(wl, 0, k)
+        assert np.array_equal(oracle.attend(L0, k, q, *c0), oracle.attend(L2, k, q, *c2))
+        # each block's stream: ceil(n_k D / cpw) words, from a fresh word
+        cpw = 32 // bits
+        W = [-(-blocks[j] * 24 // cpw) for j in range(len(blocks))]
+        assert oracle.block_word_offset(L2, k) == sum(W[:k])
+        assert oracle.nbytes(L2, n)[0] == 2 * 3 * 4 * sum(W[:n])
+
+
+def test_block_words_reproduce_the_tables_int3_rows(oracle):
+    """Per-block words at VAR-dN: 4356 words per (sequence, head), four more than
+    one stream of all 680 tokens, so 3.81 / 5.49 / 8.58 GiB and a 77.04% saving
+    beside the table's 3.81 / 5.48 / 8.57 and 77.06%."""
+    seen = 0
+    for m, layers, width, batch, method, prec, kv, saving in read_kv_table():
+        if prec != "INT3":
+            continue
+        seqs = 2 * batch
+        bf16 = _bf16_gib(layers, width, seqs, 680)
+        L = oracle.make_layout(seqs, width // 64, 64, 3, vi.VAR_BLOCKS, pack_mode=2)
+        cb, sb = oracle.nbytes(L, 10)
+        assert cb == seqs * (width // 64) * 4 * 4356
+        gib = 2 * layers * (cb + sb) / GIB
+        assert abs(gib - kv) <= 0.011, (m, gib)
+        assert round(100 * (1 - gib / bf16), 2) == 77.04
+        assert abs(100 * (1 - gib / bf16) - saving) < 0.03
+        seen += 1
+    assert seen == 3
 
 
 def test_bytes_formula_pieces(oracle):
