@@ -27,14 +27,17 @@ def cache_to_host(c):
             "scale": c["scale"].view(torch.int16).cpu().numpy().view(np.uint16)}
 
 
-def layouts(oracle, wl):
-    return (K.make_layout(wl.batch, wl.heads, wl.head_dim, wl.bits, wl.blocks),
-            oracle.layout_of(wl))
+def layouts(oracle, wl, pack_mode=0):
+    """The workload's layout for the library and for the oracle (pack_mode 0:
+    dense rows; 2: block-aligned words)."""
+    Lo = oracle.layout_of(wl)
+    Lo.pack_mode = pack_mode
+    return (K.make_layout(wl.batch, wl.heads, wl.head_dim, wl.bits, wl.blocks, pack_mode), Lo)
 
 
-def fill_both(oracle, wl, layer=0, upto=None, status=None):
+def fill_both(oracle, wl, layer=0, upto=None, status=None, pack_mode=0):
     """Quantize blocks 0..upto-1 on the GPU and in the oracle."""
-    Lg, Lo = layouts(oracle, wl)
+    Lg, Lo = layouts(oracle, wl, pack_mode)
     kg, vg = K.alloc_cache(Lg), K.alloc_cache(Lg)
     ko, vo = oracle.alloc_cache(Lo), oracle.alloc_cache(Lo)
     upto = len(wl.blocks) if upto is None else upto

@@ -189,6 +189,28 @@ def test_word_aligned_mode_bytes_and_errors(oracle):
     assert lib.kvq_attend_packed(C.byref(L), 0, FAKE, _cache(), _cache(), 0.0, FAKE, None) == U
     assert lib.kvq_quantize_attend(C.byref(L), 0, kb.BF16, FAKE, FAKE, FAKE, _cache(), _cache(),
                                    0.0, FAKE, None, None) == U
-    L.pack_mode = 2
+    L.pack_mode = 3
     with pytest.raises(K.KvqError):
         K.kvq_bytes(L, 1)
+
+
+def test_block_words_bytes_and_errors(oracle):
+    """pack_mode 2 (block-aligned words): byte accounting agrees with the oracle
+    at every width, the decode calls accept it where the kernels are built and
+    reject what they are not built for (no GPU call is made: every rejected
+    case fails in host validation)."""
+    lib = K.lib()
+    for bits in (1, 2, 3, 5, 7, 8):
+        for d in (64, 128, 24):
+            Lg = K.make_layout(3, 5, d, bits, vi.VAR_BLOCKS, pack_mode=2)
+            Lo = oracle.make_layout(3, 5, d, bits, vi.VAR_BLOCKS, pack_mode=2)
+            for n_filled in (0, 1, 7, 10):
+                assert K.kvq_bytes(Lg, n_filled) == oracle.nbytes(Lo, n_filled)
+    U = kb.E_UNSUPPORTED
+    L = K.make_layout(2, 3, 64, 5, (1, 4, 9), pack_mode=2)  # 5-bit codes: not built
+    assert lib.kvq_quantize_block(C.byref(L), 0, kb.BF16, FAKE, FAKE, _cache(), _cache(), None,
+                                  None) == U
+    assert lib.kvq_attend_packed(C.byref(L), 0, FAKE, _cache(), _cache(), 0.0, FAKE, None) == U
+    L = K.make_layout(2, 3, 64, 3, (1, 4, 9), pack_mode=2)
+    assert lib.kvq_attend_packed(C.byref(L), 0, FAKE, _cache(), _cache(), float("nan"), FAKE,
+                                 None) == kb.E_INVAL

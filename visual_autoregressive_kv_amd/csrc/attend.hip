@@ -161,6 +161,20 @@ __device__ __forceinline__ void chunk_f32(uint32_t w0, uint32_t w1, int shift, f
   }
 }
 
+// the 8 codes of a chunk of block-aligned 3-bit words: code sh / 3 of word w0
+// onward, the chunk continuing into w1 past the word's ten codes
+__device__ __forceinline__ void chunk_words3_f32(uint32_t w0, uint32_t w1, int sh, float c[8]) {
+  codes_f32<3>((w0 >> sh) | (w1 << (30 - sh)), c);
+}
+
+// Word index and bit shift of the chunk that starts at code gi of a stream of
+// block-aligned 3-bit words (gi / 10 by multiply-high: exact for 32-bit gi).
+__device__ __forceinline__ uint32_t word_of_code(uint32_t gi, int& sh) {
+  const uint32_t w = __umulhi(gi, 0xCCCCCCCDu) >> 3;
+  sh = 3 * (int)(gi - 10u * w);
+  return w;
+}
+
 // Raw buffer view of key tile j of one (b, h)'s packed prefix.  The hardware
 // range check covers the per-lane offset only (not the scalar offset), so the
 // tile's start goes into the base address and the record count is what is
@@ -199,7 +213,7 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-template <int D, int BITS, int NW, bool CHECK>
+template <int D, int BITS, int NW, bool CHECK, bool BW>
 __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, int h, int tid,
                                                   _Float16* st_lds, float* scratch,
                                                   uint8_t* stage_k, uint8_t* stage_v, int& vover) {
@@ -317,8 +331,9 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     zf[j] = zi[(tensor * 2 + 0) * kWave + 8 * c + j];
     inv[j] = zi[(tensor * 2 + 1) * kWave + 8 * c + j];
   }
-  uint8_t* dst = f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R;
-  const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
+  uint8_t* dst = BW ? f.codes[tensor] + (((int64_t)b * p.H + h) * p.bh_words + f.word_off) * 4
+                    : f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R;
+  const int mis = BW ? 0 : (int)(reinterpret_cast<uintptr_t>(dst) & 15);
   uint8_t* stg = (tensor == 0 ? stage_k : stage_v) + mis;
 #pragma unroll
   for (int i = 0; i < MAXR; ++i) {
@@ -337,7 +352,13 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
       }
     }
   }
-  if constexpr (BITS == 3) {
+  if constexpr (BW) {
+    // block-aligned words: word k of the block's stream from the dense staging
+    __syncthreads();
+    const int nc = n * D;
+    uint32_t* wd = reinterpret_cast<uint32_t*>(dst);
+    for (int k = u; k < (nc + 9) / 10; k += GT) wd[k] = word_from_dense3(stg, k, nc);
+  } else if constexpr (BITS == 3) {
     // 24-byte rows, 3 bytes per chunk, possibly 8 bytes off a 16-byte boundary:
     // the block's n * R bytes go out of LDS as 128-bit stores, byte-exact ends
     __syncthreads();
@@ -363,7 +384,9 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
 // SPLIT: the workgroup attends only key-tile range sp of p.splits (whole
 // tiles, balanced) and writes its unnormalized output, running maximum and
 // denominator to the workspace for attend_merge_kernel (attention only).
-template <int D, int BITS, int NW, int FUSE, int SPLIT = 0>
+// BW: the cache holds block-aligned 3-bit words (BITS == 3); each item's word
+// and shift are computed per tile from its key's block.
+template <int D, int BITS, int NW, int FUSE, int SPLIT = 0, bool BW = false>
 // Register caps chosen for residency: 2-wave workgroups at 3 waves per SIMD and
 // 4-wave workgroups at 4 (a few dwords spill; measured faster on VAR-d20 than
 // the extra dispatch rounds without the cap).
@@ -381,6 +404,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   __shared__ __align__(16) uint32_t v_t[2][D][VROW];  // fp16 pairs (keys 2m, 2m+1)
   extern __shared__ __align__(16) _Float16 st[];     // [blk][tensor][z|s][D] when it fits
   __shared__ int blk_end[KVQ_MAX_BLOCKS];
+  __shared__ int blk_pad[BW ? KVQ_MAX_BLOCKS : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -388,6 +412,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   const int g = lane >> 5;    // lane group: which 8 of each 16 contraction slots
   const int col = lane & 31;  // this lane's query (S^T / O^T column)
   static_assert(SPLIT == 0 || FUSE == 0, "key ranges are for the attention-only launch");
+  static_assert(!BW || BITS == 3, "block-aligned words are built for 3-bit codes");
   // fused prologue: block rows staged in k_lo (K) and v_t (V), extremes in k_hi
   static_assert(FUSE == 0 || ((BITS != 3 || (sizeof(k_lo) >= 16 + NW * 32 * BITS * D / 8 &&
                                              sizeof(v_t) >= 16 + NW * 32 * BITS * D / 8)) &&
@@ -414,8 +439,16 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   // dequantized; the statistics slot of block k in LDS is filled here, the
   // copy below skips it; the barrier after the copy publishes everything).
   int vover = 0;  // a V group's top grid level leaves the binary16 range
+  if constexpr (BW) {
+    // block ends and paddings before any load: the loads' addresses need them
+    for (int i = tid; i < nkb; i += NT) {
+      blk_end[i] = p.block_end[i];
+      blk_pad[i] = p.block_pad[i];
+    }
+    __syncthreads();
+  }
   if constexpr (FUSE != 0) {
-    quantize_block_wg<D, BITS, NW, FUSE == 2>(p, b, h, tid, st,
+    quantize_block_wg<D, BITS, NW, FUSE == 2, BW>(p, b, h, tid, st,
                                               reinterpret_cast<float*>(&k_hi[0][0][0]),
                                               reinterpret_cast<uint8_t*>(&k_lo[0][0][0]),
                                               reinterpret_cast<uint8_t*>(&v_t[0][0][0]), vover);
@@ -424,11 +457,13 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   // ---- item slots: (tensor, key, chunk), fixed for every tile ----------------
   // K items: key = rem / CPR (a row chunk); V items: key = rem % KT, so
   // neighbouring lanes hold neighbouring keys and can pair them.
-  const uint8_t* kpfx = p.kcodes + (int64_t)bh * p.T_cache * p.R;
-  const uint8_t* vpfx = p.vcodes + (int64_t)bh * p.T_cache * p.R;
-  const int pfx_bytes = n_prefix * p.R;
+  const uint8_t* kpfx = BW ? p.kcodes + (int64_t)bh * p.bh_words * 4 : p.kcodes + (int64_t)bh * p.T_cache * p.R;
+  const uint8_t* vpfx = BW ? p.vcodes + (int64_t)bh * p.bh_words * 4 : p.vcodes + (int64_t)bh * p.T_cache * p.R;
+  const int pfx_bytes = BW ? 4 * p.prefix_words : n_prefix * p.R;
   const int tile_bytes = KT * p.R;
   int s_tensor[MAXI], s_key[MAXI], s_cg[MAXI], s_voff[MAXI], s_shift[MAXI];
+  // BW: block of each item's key at its latest load, and that block's padding
+  int i_blk[MAXI], i_pad[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int it = tid + i * NT;
@@ -439,16 +474,39 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     const int byte = BITS * s_cg[i];  // chunk cg starts at byte BITS*cg of a row
     s_voff[i] = s_key[i] * p.R + (byte & ~3);
     s_shift[i] = (byte & 3) * 8;
+    i_blk[i] = 0;
+    i_pad[i] = 0;
   }
 
   // Packed bits in flight: tile j lands in register set A (j even) or B (j
   // odd) two iterations before its dequantization, so the wait for one set
   // leaves the newer set's loads outstanding.
   uint32_t preA[MAXI], pre2A[MAXI], preB[MAXI], pre2B[MAXI];
+  int shA[MAXI], shB[MAXI];  // BW: bit shift of each item's chunk in its first word
   // fused launch: block k's rows are written below; tile 0 is fetched before
-  // that only if it ends before block k, tile 1 always after
+  // that only if it ends before block k, tile 1 always after (block-aligned
+  // words: a chunk ending in the last word of block k - 1 also loads block k's
+  // first word, whose bits it does not use)
   const bool early0 = FUSE == 0 || (int)p.fz.off >= KT;
-  auto issue_loads = [&](int j, uint32_t (&pre)[MAXI], uint32_t (&pre2)[MAXI]) {
+  auto issue_loads = [&](int j, uint32_t (&pre)[MAXI], uint32_t (&pre2)[MAXI], int (&sh)[MAXI]) {
+    if constexpr (BW) {
+      // the whole prefix in one view: loads past its words return 0
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpfx, pfx_bytes, 0, 0);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpfx, pfx_bytes, 0, 0);
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) {
+        const int t = j * KT + s_key[i];
+        while (i_blk[i] + 1 < nkb && t >= blk_end[i_blk[i]]) {  // keys only move forward
+          ++i_blk[i];
+          i_pad[i] = blk_pad[i_blk[i]];
+        }
+        const int voff = 4 * (int)word_of_code((uint32_t)(t * D + 8 * s_cg[i] + i_pad[i]), sh[i]);
+        const __amdgpu_buffer_rsrc_t r = s_tensor[i] == 0 ? rk : rv;
+        pre[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+        pre2[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4, 0, 0);
+      }
+      return;
+    }
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpfx, pfx_bytes, tile_bytes, j);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpfx, pfx_bytes, tile_bytes, j);
 #pragma unroll
@@ -461,10 +519,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
         pre2[i] = 0u;
     }
   };
-  if (early0) issue_loads(j_begin, preA, pre2A);
+  if (early0) issue_loads(j_begin, preA, pre2A, shA);
 
   // ---- block ends and statistics to LDS, Q operand to registers -------------
-  for (int i = tid; i < nkb; i += NT) blk_end[i] = p.block_end[i];
+  if constexpr (!BW)
+    for (int i = tid; i < nkb; i += NT) blk_end[i] = p.block_end[i];
   {  // 8 binary16 values per copy; a fused launch writes block k's
     const int nkb_copy = FUSE != 0 ? nkb - 1 : nkb;
     for (int i = tid; i < nkb_copy * 2 * CPR; i += NT) {
@@ -494,8 +553,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   // blk_end, statistics and (fused) block k's rows visible; every workgroup of
   // a (sequence, head) sees the same statistics, so key ranges agree on vhalf
   const bool vhalf = __syncthreads_or(vover) != 0;
-  if (!early0) issue_loads(j_begin, preA, pre2A);
-  issue_loads(j_begin + 1, preB, pre2B);  // no records past the prefix: reads nothing
+  if (!early0) issue_loads(j_begin, preA, pre2A, shA);
+  issue_loads(j_begin + 1, preB, pre2B, shB);  // no records past the prefix: reads nothing
 
   // binary16 statistics (8 channels of z and s) of one block for one tensor,
   // from LDS only (a read that may also go to global memory compiles to a flat
@@ -516,7 +575,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
     load_stats(0, s_tensor[i], s_cg[i], s_z[i], s_s[i]);
   }
 
-  auto dequant = [&](int j, int buf, const uint32_t (&pre)[MAXI], const uint32_t (&pre2)[MAXI]) {
+  auto dequant = [&](int j, int buf, const uint32_t (&pre)[MAXI], const uint32_t (&pre2)[MAXI],
+                     const int (&sh)[MAXI]) {
     const int t0 = j * KT;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
@@ -532,7 +592,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       // keys past the prefix read codes 0 (buffer range check) and keep the
       // last block's statistics: finite values whose scores are masked out
       float cf[8], x[8];
-      chunk_f32<BITS>(pre[i], pre2[i], s_shift[i], cf);
+      if constexpr (BW)
+        chunk_words3_f32(pre[i], pre2[i], sh[i], cf);
+      else
+        chunk_f32<BITS>(pre[i], pre2[i], s_shift[i], cf);
 #pragma unroll
       for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf(cf[c], (float)s_s[i][c], (float)s_z[i][c]);
       if (s_tensor[i] != 0 && vhalf) {
@@ -585,17 +648,18 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   float l_run = 0.0f;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  dequant(j_begin, 0, preA, pre2A);
+  dequant(j_begin, 0, preA, pre2A, shA);
   __syncthreads();
 
   // tile j: cur holds tile j+1's packed bits (issued one iteration earlier),
   // tile j+2's loads go into nxt
   auto step = [&](int j, const uint32_t (&cur)[MAXI], const uint32_t (&cur2)[MAXI],
-                  uint32_t (&nxt)[MAXI], uint32_t (&nxt2)[MAXI]) {
+                  const int (&cursh)[MAXI], uint32_t (&nxt)[MAXI], uint32_t (&nxt2)[MAXI],
+                  int (&nxtsh)[MAXI]) {
     const int t0 = j * KT;
     const int buf = (j - j_begin) & 1;
     const bool has_next = j + 1 < j_end;
-    issue_loads(j + 2, nxt, nxt2);  // unconditional: past the prefix it reads nothing
+    issue_loads(j + 2, nxt, nxt2, nxtsh);  // unconditional: past the prefix it reads nothing
 
     if (wave_live) {
       // ---- S^T = K_hat Q^T -------------------------------------------------
@@ -621,7 +685,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // the next tile's dequantization runs while these MFMAs complete
-      if (has_next) dequant(j + 1, buf ^ 1, cur, cur2);
+      if (has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
 
       // ---- online softmax (log2 domain) -----------------------------------
       if (t0 + KT > n_prefix) {
@@ -674,15 +738,15 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
       }
     }
 
-    if (!wave_live && has_next) dequant(j + 1, buf ^ 1, cur, cur2);
+    if (!wave_live && has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
     __syncthreads();
   };
   int j = j_begin;
   for (; j + 1 < j_end; j += 2) {
-    step(j, preB, pre2B, preA, pre2A);
-    step(j + 1, preA, pre2A, preB, pre2B);
+    step(j, preB, pre2B, shB, preA, pre2A, shA);
+    step(j + 1, preA, pre2A, shA, preB, pre2B, shB);
   }
-  if (j < j_end) step(j, preB, pre2B, preA, pre2A);
+  if (j < j_end) step(j, preB, pre2B, shB, preA, pre2A, shA);
 
   const float l_tot = sum_xor32(l_run);
   const float oscale = vhalf ? 2.0f : 1.0f;  // undo the v_hat halving
@@ -744,7 +808,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
 template <int BITS>
 constexpr int kFusedRowBytes = BITS == 8 ? 64 : 32;
 
-template <int D, int BITS, bool F32, bool CHECK>
+template <int D, int BITS, bool F32, bool CHECK, bool BW>
 __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b, int h, int lane,
                                                     _Float16* st_lds, uint8_t* rows_lds,
                                                     float* scratch, int& vover) {
@@ -822,11 +886,18 @@ __device__ __forceinline__ void quantize_block_wave(const AttendParams& p, int b
           }
         }
         const Packed8 pk = pack_chunk<BITS>(x, zf, inv);
-        store_chunk<BITS>(rows + (int64_t)t * p.R + BITS * cg, pk);
+        if constexpr (!BW) store_chunk<BITS>(rows + (int64_t)t * p.R + BITS * cg, pk);
         store_chunk<BITS>(lrows + t * p.R + BITS * cg, pk);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // scratch reuse
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // scratch reuse, LDS rows written
+    if constexpr (BW) {
+      // the LDS rows are the block's dense stream: its words, one per lane
+      uint32_t* wd = reinterpret_cast<uint32_t*>(
+          f.codes[tensor] + (((int64_t)b * p.H + h) * p.bh_words + f.word_off) * 4);
+      const int nc = n * D;
+      for (int k = lane; k < (nc + 9) / 10; k += kWave) wd[k] = word_from_dense3(lrows, k, nc);
+    }
   }
   if constexpr (CHECK) {
     if (flags) atomicOr(f.status, flags);
@@ -848,7 +919,10 @@ constexpr int kSmallStatsHalves = 2048;  // 4 KB per wave: up to 8 blocks at hea
 
 // FUSE: 0 attention only; 1/2 quantize the block first from bf16 (2: with
 // input checks); 3/4 the same from fp32.
-template <int D, int BITS, int QT, int FUSE>
+// BW: block-aligned 3-bit words (BITS == 3), addressed per tile from the
+// lane's key's block; block k's rows in a fused launch still come from LDS in
+// the dense row form.
+template <int D, int BITS, int QT, int FUSE, bool BW = false>
 // 3 waves per SIMD: with 4-wave workgroups every VAR-d20 (sequence, head) is
 // resident in one dispatch round
 __global__ __launch_bounds__(kSmallWaves * kWave)
@@ -860,6 +934,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   __shared__ __align__(16) uint32_t v_t_all[kSmallWaves][D][VROW];
   __shared__ __align__(16) _Float16 st_all[kSmallWaves][kSmallStatsHalves];
   __shared__ int bend_all[kSmallWaves][KVQ_MAX_BLOCKS];
+  __shared__ int bpad_all[kSmallWaves][BW ? KVQ_MAX_BLOCKS : 1];
+  static_assert(!BW || BITS == 3, "block-aligned words are built for 3-bit codes");
   // fused launch: the packed rows of block k (K then V) for the attention below
   __shared__ __align__(16) uint8_t rows_all[kSmallWaves][FUSE != 0 ? 2 * KT * kFusedRowBytes<BITS> : 16];
 
@@ -873,6 +949,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   uint32_t(*v_t)[VROW] = v_t_all[wave];
   _Float16* st = st_all[wave];  // [blk][tensor][z|s][D]
   int* bend = bend_all[wave];
+  int* bpad = bpad_all[wave];
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int nkb = p.n_kblocks;
@@ -880,9 +957,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   const int n_tiles = (n_prefix + KT - 1) / KT;
   const int64_t stat_base = (int64_t)bh * p.NB * D;
 
-  const uint8_t* kpfx = p.kcodes + (int64_t)bh * p.T_cache * p.R;
-  const uint8_t* vpfx = p.vcodes + (int64_t)bh * p.T_cache * p.R;
-  const int pfx_bytes = n_prefix * p.R;
+  const uint8_t* kpfx = BW ? p.kcodes + (int64_t)bh * p.bh_words * 4 : p.kcodes + (int64_t)bh * p.T_cache * p.R;
+  const uint8_t* vpfx = BW ? p.vcodes + (int64_t)bh * p.bh_words * 4 : p.vcodes + (int64_t)bh * p.T_cache * p.R;
+  const int pfx_bytes = BW ? 4 * p.prefix_words : n_prefix * p.R;
   const int tile_bytes = KT * p.R;
   // K: this lane's key is `col`, its chunks are 2 ks + g; V items: key = it % KT
   int k_voff[KS], k_shift[KS], v_key[VI], v_cg[VI], v_voff[VI], v_shift[VI];
@@ -902,7 +979,38 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
     v_shift[i] = (byte & 3) * 8;
   }
   uint32_t kpre[KS][2], vpre[VI][2];
+  // BW: V item i is chunk 2 i + g of key `col`, the same chunk as K k-step i,
+  // so one word index and shift serve both tensors
+  static_assert(VI == KS, "V items and K k-steps pair up");
+  int wsh_pre[KS] = {};
+  int ib = 0, ipad = 0;  // BW: block of this lane's key at its latest load, its padding
+  if constexpr (BW) {
+    if (lane < nkb) {
+      bend[lane] = p.block_end[lane];
+      bpad[lane] = p.block_pad[lane];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
   auto issue_loads = [&](int j) {
+    if constexpr (BW) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpfx, pfx_bytes, 0, 0);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpfx, pfx_bytes, 0, 0);
+      const int t = j * KT + col;
+      while (ib + 1 < nkb && t >= bend[ib]) {
+        ++ib;
+        ipad = bpad[ib];
+      }
+      const uint32_t gi0 = (uint32_t)(t * D + 8 * g + ipad);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int voff = 4 * (int)word_of_code(gi0 + 16u * ks, wsh_pre[ks]);
+        kpre[ks][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, voff, 0, 0);
+        kpre[ks][1] = __builtin_amdgcn_raw_buffer_load_b32(rk, voff + 4, 0, 0);
+        vpre[ks][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, 0, 0);
+        vpre[ks][1] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + 4, 0, 0);
+      }
+      return;
+    }
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpfx, pfx_bytes, tile_bytes, j);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpfx, pfx_bytes, tile_bytes, j);
 #pragma unroll
@@ -935,7 +1043,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
     *reinterpret_cast<u32x4*>(row + D) = sw;
     if (tensor == 1) vover |= v_top_over_f16<BITS>(zw, sw);
   }
-  if (lane < nkb) bend[lane] = p.block_end[lane];
+  if (!BW && lane < nkb) bend[lane] = p.block_end[lane];
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   bf16x8 qop[QT][KS];
 #pragma unroll
@@ -955,7 +1063,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   // Rows of block k then come from LDS (keys off .. off + n - 1).
   const uint8_t* qrows = rows_all[wave];
   if constexpr (FUSE != 0)
-    quantize_block_wave<D, BITS, FUSE >= 3, FUSE == 2 || FUSE == 4>(
+    quantize_block_wave<D, BITS, FUSE >= 3, FUSE == 2 || FUSE == 4, BW>(
         p, b, h, lane, st, rows_all[wave], reinterpret_cast<float*>(&v_t[0][0]), vover);
   const bool vhalf = __any(vover);
 
@@ -986,10 +1094,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   for (int j = 0; j < n_tiles; ++j) {
     const int t0 = j * KT;
     uint32_t kc[KS][2], vc[VI][2];
+    int wsh[KS];  // BW: shifts of this tile's chunks
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kc[ks][0] = kpre[ks][0];
       kc[ks][1] = kpre[ks][1];
+      wsh[ks] = wsh_pre[ks];
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
@@ -1018,6 +1128,17 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
           vc[i][0] = *reinterpret_cast<const uint32_t*>(vr + bo);
           if constexpr (kTwoWords<BITS>) vc[i][1] = *reinterpret_cast<const uint32_t*>(vr + bo + 4);
         }
+        if constexpr (BW) {
+          // dense LDS rows: the chunk's 24 bits as a word read from bit 0
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            kc[ks][0] = (uint32_t)(((uint64_t)kc[ks][1] << 32 | kc[ks][0]) >> k_shift[ks]);
+            kc[ks][1] = 0u;
+            vc[ks][0] = (uint32_t)(((uint64_t)vc[ks][1] << 32 | vc[ks][0]) >> v_shift[ks]);
+            vc[ks][1] = 0u;
+            wsh[ks] = 0;
+          }
+        }
       }
     }
     while (tk >= blk_next) {
@@ -1033,7 +1154,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
       f16x8 z, sc;
       stats(1, v_cg[i], z, sc);
       float cf[8], x[8];
-      chunk_f32<BITS>(vc[i][0], vc[i][1], v_shift[i], cf);
+      if constexpr (BW)
+        chunk_words3_f32(vc[i][0], vc[i][1], wsh[i], cf);
+      else
+        chunk_f32<BITS>(vc[i][0], vc[i][1], v_shift[i], cf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
       if (vhalf) {
@@ -1066,7 +1190,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
         f16x8 z, sc;
         stats(0, 2 * ks + g, z, sc);
         float cf[8], x[8];
-        chunk_f32<BITS>(kc[ks][0], kc[ks][1], k_shift[ks], cf);
+        if constexpr (BW)
+          chunk_words3_f32(kc[ks][0], kc[ks][1], wsh[ks], cf);
+        else
+          chunk_f32<BITS>(kc[ks][0], kc[ks][1], k_shift[ks], cf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(cf[e], (float)sc[e], (float)z[e]);
         u32x4 hi, lo;
@@ -1166,18 +1293,18 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attend_small_kernel(A
   }
 }
 
-template <int D, int BITS, int QT, int FUSE = 0>
+template <int D, int BITS, int QT, int FUSE = 0, bool BW = false>
 hipError_t launch_small(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = 1;
   const int64_t grid = ((int64_t)p.B * p.H + kSmallWaves - 1) / kSmallWaves;
   if (!dispatch_fits(grid, kSmallWaves * kWave)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attend_small_kernel<D, BITS, QT, FUSE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attend_small_kernel<D, BITS, QT, FUSE, BW>), dim3((unsigned)grid),
                      dim3(kSmallWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, int BITS, int NW, int FUSE = 0, int SPLIT = 0>
+template <int D, int BITS, int NW, int FUSE = 0, int SPLIT = 0, bool BW = false>
 hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   AttendParams a = p;
   a.q_tiles = (p.n + NW * 32 - 1) / (NW * 32);
@@ -1186,22 +1313,23 @@ hipError_t launch_nw(const AttendParams& p, hipStream_t s) {
   const size_t dyn = (size_t)p.n_kblocks * 4 * D * sizeof(_Float16);
   const int64_t grid = (int64_t)p.B * p.H * a.q_tiles * (SPLIT ? p.splits : 1);
   if (!dispatch_fits(grid, NW * kWave)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE, SPLIT>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attend_kernel<D, BITS, NW, FUSE, SPLIT, BW>), dim3((unsigned)grid),
                      dim3(NW * kWave), dyn, s, a);
   return hipGetLastError();
 }
 
 // waves per workgroup: enough 32-query waves for the block, rounded to 1/2/4/8
-template <int D, int BITS>
+template <int D, int BITS, bool BW = false>
 hipError_t launch_t(const AttendParams& p, hipStream_t s) {
   // Up to 32 queries the one-wave kernel wins; from 33 on, measured on VAR-d20,
   // sharing each tile's dequantization among the block's waves does better.
-  if (p.n <= 32 && p.n_kblocks * 4 * D <= kSmallStatsHalves) return launch_small<D, BITS, 1>(p, s);
+  if (p.n <= 32 && p.n_kblocks * 4 * D <= kSmallStatsHalves)
+    return launch_small<D, BITS, 1, 0, BW>(p, s);
   const int waves = (min(p.n, kMaxWaves * 32) + 31) / 32;
-  if (waves <= 1) return launch_nw<D, BITS, 1>(p, s);
-  if (waves <= 2) return launch_nw<D, BITS, 2>(p, s);
-  if (waves <= 4) return launch_nw<D, BITS, 4>(p, s);
-  return launch_nw<D, BITS, 8>(p, s);
+  if (waves <= 1) return launch_nw<D, BITS, 1, 0, 0, BW>(p, s);
+  if (waves <= 2) return launch_nw<D, BITS, 2, 0, 0, BW>(p, s);
+  if (waves <= 4) return launch_nw<D, BITS, 4, 0, 0, BW>(p, s);
+  return launch_nw<D, BITS, 8, 0, 0, BW>(p, s);
 }
 
 }  // namespace
@@ -1222,7 +1350,17 @@ hipError_t launch_t(const AttendParams& p, hipStream_t s) {
     }                                                   \
   } while (0)
 
+// block-aligned 3-bit words: launcher template L<D, 3, true>
+#define KVQ_DISPATCH_WORDS(L, head_dim, bits, ...)         \
+  do {                                                     \
+    if ((bits) != 3) return hipErrorInvalidValue;          \
+    if ((head_dim) == 64) return L<64, 3, true>(__VA_ARGS__); \
+    if ((head_dim) == 128) return L<128, 3, true>(__VA_ARGS__); \
+    return hipErrorInvalidValue;                           \
+  } while (0)
+
 hipError_t launch_attend(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
+  if (p.word_layout) KVQ_DISPATCH_WORDS(launch_t, head_dim, bits, p, s);
   KVQ_DISPATCH(launch_t, head_dim, bits, p, s);
 }
 
@@ -1255,11 +1393,11 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendParams p) {
       f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool BW = false>
 hipError_t launch_split_t(const AttendParams& p, hipStream_t s) {
   const int64_t merge_grid = (p.ws_rows * (D / 4) + 255) / 256;
   if (!dispatch_fits(merge_grid, 256)) return hipErrorInvalidConfiguration;
-  const hipError_t e = launch_nw<D, BITS, kMaxWaves, 0, 1>(p, s);
+  const hipError_t e = launch_nw<D, BITS, kMaxWaves, 0, 1, BW>(p, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)merge_grid), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -1267,14 +1405,16 @@ hipError_t launch_split_t(const AttendParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attend_split(const AttendParams& p, int head_dim, int bits, hipStream_t s) {
+  if (p.word_layout) KVQ_DISPATCH_WORDS(launch_split_t, head_dim, bits, p, s);
   KVQ_DISPATCH(launch_split_t, head_dim, bits, p, s);
 }
 
 namespace {
-template <int BITS>
+template <int BITS, bool BW = false>
 hipError_t launch_small_fused(const AttendParams& a, bool f32, bool check, hipStream_t s) {
-  if (f32) return check ? launch_small<64, BITS, 1, 4>(a, s) : launch_small<64, BITS, 1, 3>(a, s);
-  return check ? launch_small<64, BITS, 1, 2>(a, s) : launch_small<64, BITS, 1, 1>(a, s);
+  if (f32)
+    return check ? launch_small<64, BITS, 1, 4, BW>(a, s) : launch_small<64, BITS, 1, 3, BW>(a, s);
+  return check ? launch_small<64, BITS, 1, 2, BW>(a, s) : launch_small<64, BITS, 1, 1, BW>(a, s);
 }
 }  // namespace
 
@@ -1288,13 +1428,16 @@ static void fill_fuse(AttendParams& p, const QuantParams& q) {
   p.fz.status = q.status;
   p.fz.off = q.off;
   p.fz.block = q.block;
+  p.fz.word_off = q.word_off;
 }
 
-template <int BITS>
+template <int BITS, bool BW = false>
 static hipError_t launch_wg_fused(const AttendParams& p, int waves, bool check, hipStream_t s) {
-  if (waves <= 2) return check ? launch_nw<64, BITS, 2, 2>(p, s) : launch_nw<64, BITS, 2, 1>(p, s);
-  if (waves <= 4) return check ? launch_nw<64, BITS, 4, 2>(p, s) : launch_nw<64, BITS, 4, 1>(p, s);
-  return check ? launch_nw<64, BITS, 8, 2>(p, s) : launch_nw<64, BITS, 8, 1>(p, s);
+  if (waves <= 2)
+    return check ? launch_nw<64, BITS, 2, 2, 0, BW>(p, s) : launch_nw<64, BITS, 2, 1, 0, BW>(p, s);
+  if (waves <= 4)
+    return check ? launch_nw<64, BITS, 4, 2, 0, BW>(p, s) : launch_nw<64, BITS, 4, 1, 0, BW>(p, s);
+  return check ? launch_nw<64, BITS, 8, 2, 0, BW>(p, s) : launch_nw<64, BITS, 8, 1, 0, BW>(p, s);
 }
 
 hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,
@@ -1304,6 +1447,8 @@ hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, i
     AttendParams p = a;
     fill_fuse(p, q);
     const bool check = q.status != nullptr;
+    if (a.word_layout)
+      return bits == 3 ? launch_small_fused<3, true>(p, f32src, check, s) : hipErrorInvalidValue;
     switch (bits) {
       case 2: return launch_small_fused<2>(p, f32src, check, s);
       case 3: return launch_small_fused<3>(p, f32src, check, s);
@@ -1318,6 +1463,8 @@ hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, i
     AttendParams p = a;
     fill_fuse(p, q);
     const bool check = q.status != nullptr;
+    if (a.word_layout)
+      return bits == 3 ? launch_wg_fused<3, true>(p, waves, check, s) : hipErrorInvalidValue;
     switch (bits) {
       case 2: return launch_wg_fused<2>(p, waves, check, s);
       case 3: return launch_wg_fused<3>(p, waves, check, s);

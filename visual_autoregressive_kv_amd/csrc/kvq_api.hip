@@ -25,7 +25,7 @@ int validate_layout(const kvq_layout* L) {
   if (L->head_dim < 8 || L->head_dim % 8 != 0) return KVQ_E_INVAL;
   if (L->bits < 1 || L->bits > 8) return KVQ_E_INVAL;
   if (L->n_blocks < 1 || L->n_blocks > KVQ_MAX_BLOCKS) return KVQ_E_INVAL;
-  if (L->pack_mode != 0 && L->pack_mode != 1) return KVQ_E_INVAL;
+  if (L->pack_mode < 0 || L->pack_mode > 2) return KVQ_E_INVAL;
   int64_t T = 0;
   for (int i = 0; i < L->n_blocks; ++i) {
     if (L->block_tokens[i] < 1) return KVQ_E_INVAL;
@@ -38,15 +38,35 @@ int validate_layout(const kvq_layout* L) {
   return KVQ_OK;
 }
 
+// Block-aligned words (pack_mode 2): words of blocks 0..block-1 in one (b, h)
+// cache, each block's n_k * D codes in ceil(n_k * D / floor(32 / bits)) words.
+int64_t words_before(const kvq_layout* L, int32_t block) {
+  const int64_t cpw = 32 / L->bits;
+  int64_t w = 0;
+  for (int i = 0; i < block; ++i) w += ((int64_t)L->block_tokens[i] * L->head_dim + cpw - 1) / cpw;
+  return w;
+}
+
+// pack_mode 2 with a width whose codes do not fill 32 bits (3 on the GPU): the
+// kernels' word layout.  With 2-, 4- and 8-bit codes and head_dim a multiple of
+// 64 every block's stream fills whole words and equals its dense rows byte for
+// byte, so those run the dense-row kernels unchanged.
+bool word_layout(const kvq_layout* L) { return L->pack_mode == 2 && 32 % L->bits != 0; }
+
 // kernels are built for 2/3/4/8-bit codes and head_dim 64/128
 int gpu_supported(const kvq_layout* L) {
-  if (L->pack_mode != 0) return KVQ_E_UNSUPPORTED;  // the decode path keeps dense rows
+  if (L->pack_mode == 1) return KVQ_E_UNSUPPORTED;  // one stream per (b, h): not block-writable
   if (L->bits != 2 && L->bits != 3 && L->bits != 4 && L->bits != 8) return KVQ_E_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return KVQ_E_UNSUPPORTED;
-  // one (b, h)'s rows are addressed with 32-bit buffer offsets
+  // one (b, h)'s codes are addressed with 32-bit buffer offsets; block-aligned
+  // words also with 32-bit code indices (plus a few tiles past the prefix)
   int64_t T = 0;
   for (int i = 0; i < L->n_blocks; ++i) T += L->block_tokens[i];
   if (T * row_bytes(L->bits, L->head_dim) > INT32_MAX) return KVQ_E_UNSUPPORTED;
+  if (word_layout(L)) {
+    const int64_t W = words_before(L, L->n_blocks) + 4096;
+    if (4 * W > INT32_MAX || 10 * W > (int64_t)UINT32_MAX) return KVQ_E_UNSUPPORTED;
+  }
   return KVQ_OK;
 }
 
@@ -79,7 +99,8 @@ int device_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE
 // threads per (tensor, b, h) tile and rows per thread for a block of n rows:
 // the smallest power-of-two group (>= one row of chunks) that covers the block
 // with at most 8 rows per thread; larger blocks stream in passes of 256 x 8
-void pick_tiling(int n, int d, int32_t* gs, int32_t* rpt) {
+// (256 x 5 for block-aligned words, so that each pass starts on a word)
+void pick_tiling(int n, int d, bool words, int32_t* gs, int32_t* rpt) {
   const int cpr = d / 8;
   for (int g = cpr; g <= 256; g <<= 1) {
     const int rps = g / cpr;
@@ -91,7 +112,7 @@ void pick_tiling(int n, int d, int32_t* gs, int32_t* rpt) {
     }
   }
   *gs = 256;
-  *rpt = 8;
+  *rpt = words ? 5 : 8;
 }
 
 // argument checks and launch descriptor of kvq_quantize_block
@@ -127,7 +148,12 @@ int make_quant_params(const kvq_layout* layout, int32_t block, int32_t src_dtype
   p.R = row_bytes(layout->bits, layout->head_dim);
   p.T = offset_of(layout, layout->n_blocks);
   p.off = offset_of(layout, block);
-  pick_tiling(p.n, layout->head_dim, &p.gs, &p.rpt);
+  p.word_layout = word_layout(layout);
+  if (p.word_layout) {
+    p.bh_words = words_before(layout, layout->n_blocks);
+    p.word_off = words_before(layout, block);
+  }
+  pick_tiling(p.n, layout->head_dim, p.word_layout, &p.gs, &p.rpt);
   return KVQ_OK;
 }
 
@@ -167,6 +193,14 @@ int make_attend_params(const kvq_layout* layout, int32_t block, const uint16_t* 
   for (int i = 0; i < layout->n_blocks; ++i) {
     e += layout->block_tokens[i];
     p.block_end[i] = (int32_t)e;
+  }
+  p.word_layout = word_layout(layout);
+  if (p.word_layout) {
+    const int64_t cpw = 32 / layout->bits;
+    p.bh_words = words_before(layout, layout->n_blocks);
+    p.prefix_words = (int32_t)words_before(layout, block + 1);
+    for (int i = 0; i < layout->n_blocks; ++i)
+      p.block_pad[i] = (int32_t)(cpw * words_before(layout, i) - layout->head_dim * offset_of(layout, i));
   }
   return KVQ_OK;
 }
@@ -245,6 +279,8 @@ int kvq_bytes(const kvq_layout* layout, int32_t n_filled, uint64_t* code_bytes,
     const uint64_t cpw = 32u / (uint64_t)layout->bits;
     const uint64_t n = T * (uint64_t)layout->head_dim;
     *code_bytes = bh * 4u * ((n + cpw - 1) / cpw);
+  } else if (layout->pack_mode == 2) {  // one word-aligned stream per (b, h, block)
+    *code_bytes = bh * 4u * (uint64_t)words_before(layout, n_filled);
   } else {
     *code_bytes = bh * T * (uint64_t)row_bytes(layout->bits, layout->head_dim);
   }
@@ -347,6 +383,13 @@ int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const c
   for (int i = 0; i < layout->n_blocks; ++i) {
     e += layout->block_tokens[i];
     p.block_end[i] = (int32_t)e;
+  }
+  p.word_layout = word_layout(layout);
+  if (p.word_layout) {
+    p.bh_words = words_before(layout, layout->n_blocks);
+    for (int i = 0; i < layout->n_blocks; ++i)
+      p.block_pad[i] = (int32_t)((32 / layout->bits) * words_before(layout, i) -
+                                 layout->head_dim * offset_of(layout, i));
   }
   p.n_chunks = (int64_t)layout->batch * layout->heads * p.T_out * (p.D / 8);
   return device_status(launch_dequantize(p, stream));

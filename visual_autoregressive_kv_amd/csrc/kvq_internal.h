@@ -177,9 +177,26 @@ __device__ __forceinline__ void store_chunk(uint8_t* dst, const Packed8& v) {
   }
 }
 
+// Block-aligned 3-bit words: each (sequence, head, block) stream of n_k x D
+// codes, row after row, in 32-bit words of ten codes (code k of a word at bits
+// [3k, 3k + 3), the top two bits zero), every block from a fresh word.  Word w
+// of a stream is bits [30 w, 30 w + 30) of the same codes packed densely (code
+// i at bit 3 i), which is how the quantizers form it from their LDS staging.
+// dense: 4-byte aligned, readable 8 bytes past the n_codes codes; codes past
+// n_codes come out zero.
+__device__ __forceinline__ uint32_t word_from_dense3(const uint8_t* dense, int w, int n_codes) {
+  const int bit = 30 * w;
+  const uint32_t* d32 = reinterpret_cast<const uint32_t*>(dense);
+  const uint64_t both = (uint64_t)d32[bit >> 5] | ((uint64_t)d32[(bit >> 5) + 1] << 32);
+  uint32_t v = (uint32_t)(both >> (bit & 31)) & 0x3FFFFFFFu;
+  const int left = n_codes - 10 * w;
+  if (left < 10) v &= (1u << (3 * left)) - 1u;
+  return v;
+}
+
 struct QuantParams {
   const void* src[2];  // K, V: [B][n][H][D]
-  uint8_t* codes[2];   // [B][H][T][R]
+  uint8_t* codes[2];   // [B][H][T][R]; block-aligned words: [B][H][bh_words] words
   uint16_t* zero[2];   // [B][H][NB][D]
   uint16_t* scale[2];
   int32_t* status;     // nullable
@@ -189,7 +206,16 @@ struct QuantParams {
   int32_t BH, H, n, NB, block, R;
   int32_t gs;          // threads per (tensor, b, h) tile
   int32_t rpt;         // rows per thread per pass
+  int32_t word_layout; // block-aligned 3-bit words (then R is still the dense row size)
+  int64_t bh_words;    // words per (b, h) cache (word layout)
+  int64_t word_off;    // first word of the block in each (b, h) cache (word layout)
 };
+
+// the block's packed codes in the cache of (tensor kv, b*H + h)
+__device__ __forceinline__ uint8_t* block_codes(const QuantParams& p, int kv, int64_t bh) {
+  return p.word_layout ? p.codes[kv] + (bh * p.bh_words + p.word_off) * 4
+                       : p.codes[kv] + (bh * p.T + p.off) * p.R;
+}
 
 // a dispatch holds at most 2^32 - 1 work-items
 inline bool dispatch_fits(int64_t groups, int threads) {
@@ -227,6 +253,9 @@ struct DequantParams {
   int32_t H, D, bits, R, NB;
   int32_t n_filled;
   int32_t block_end[KVQ_MAX_BLOCKS];  // exclusive prefix ends
+  int32_t word_layout;                // block-aligned 3-bit words
+  int64_t bh_words;
+  int32_t block_pad[KVQ_MAX_BLOCKS];  // word layout: padding codes before block k
 };
 
 // Quantize-and-pack side of the fused quantize + attend launch: block `block`
@@ -240,6 +269,7 @@ struct FuseParams {
   int32_t* status;  // nullable
   int64_t off;
   int32_t block;
+  int64_t word_off;  // block-aligned words: the block's first word
 };
 
 struct AttendParams {
@@ -258,6 +288,15 @@ struct AttendParams {
   int32_t q_tiles;    // query tiles per (b, h)
   float scale_log2;   // softmax scale * log2(e)
   int32_t block_end[KVQ_MAX_BLOCKS];
+  // Block-aligned 3-bit words: each (b, h) cache holds bh_words words, the
+  // prefix's blocks prefix_words of them; code (t, d) of a key t in block k
+  // is code t D + d + block_pad[k] of the (b, h) stream, block_pad[k] = 10 W_k
+  // - D off_k being the padding codes that the word boundaries of blocks
+  // 0..k-1 add (W_k: words before block k).
+  int32_t word_layout;
+  int32_t prefix_words;
+  int64_t bh_words;
+  int32_t block_pad[KVQ_MAX_BLOCKS];
   FuseParams fz;  // used by the fused launch only
   // key-range launch only: ranges per query tile and the partials'
   // workspace, ws_o [splits][rows][D] and ws_ml [splits][rows][2] (rows = B n H)

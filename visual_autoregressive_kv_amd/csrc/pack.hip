@@ -95,9 +95,20 @@ __global__ __launch_bounds__(kWG) void dequant_kernel(DequantParams p) {
   const int64_t t = rowid - bh * p.T_out;
   int k = 0;
   while (k < p.n_filled - 1 && t >= p.block_end[k]) ++k;
-  const uint8_t* row = p.codes + (bh * p.T_cache + t) * p.R + (int64_t)cg * p.bits;
   uint64_t w = 0;
-  for (int j = 0; j < p.bits; ++j) w |= (uint64_t)row[j] << (8 * j);
+  if (p.word_layout) {
+    // block-aligned 3-bit words: the chunk starts at code gi of the (b, h)
+    // stream and runs into the next word when fewer than 8 codes are left
+    const uint32_t gi = (uint32_t)(t * p.D + 8 * cg + p.block_pad[k]);
+    const uint32_t wi = gi / 10u;
+    const int r = (int)(gi - 10u * wi);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(p.codes) + bh * p.bh_words;
+    w = words[wi] >> (3 * r);
+    if (r > 2) w |= (uint64_t)words[wi + 1] << (30 - 3 * r);
+  } else {
+    const uint8_t* row = p.codes + (bh * p.T_cache + t) * p.R + (int64_t)cg * p.bits;
+    for (int j = 0; j < p.bits; ++j) w |= (uint64_t)row[j] << (8 * j);
+  }
   const uint32_t mask = (1u << p.bits) - 1u;
   const int64_t so = (bh * p.NB + k) * p.D + 8 * cg;
   float* out = p.out + rowid * p.D + 8 * cg;

@@ -124,13 +124,17 @@ __device__ __forceinline__ void extremes8(const Chunk<F32> (&v)[kMaxRpt], int nv
 // Codes of the register rows of one pass, staged in LDS with the destination's
 // 16-byte misalignment, then written with 128-bit stores plus byte-exact head
 // and tail.  Every thread of the workgroup calls it (one barrier inside).
-template <int D, int BITS, bool F32>
+// BW (block-aligned 3-bit words): the pass starts on a word of the block's
+// stream (a pass holds a multiple of 5 rows of 64 or 128 codes, i.e. of ten
+// codes) and its words are formed from the dense staging, one per thread.
+template <int D, int BITS, bool F32, bool BW>
 __device__ __forceinline__ void pack_store(const Chunk<F32> (&v)[kMaxRpt], int nvalid, int r0, int rps,
                                            int cg, const float (&zf)[8], const float (&inv)[8],
                                            uint8_t* my_stage, uint8_t* dst, int rows_here, int R,
                                            int lt, int gs) {
+  static_assert(!BW || BITS == 3, "block-aligned words are built for 3-bit codes");
   constexpr int CPR = D / 8;
-  const int mis = (int)(reinterpret_cast<uintptr_t>(dst) & 15);
+  const int mis = BW ? 0 : (int)(reinterpret_cast<uintptr_t>(dst) & 15);
 #pragma unroll
   for (int i = 0; i < kMaxRpt; ++i) {
     if (i < nvalid) {
@@ -142,6 +146,12 @@ __device__ __forceinline__ void pack_store(const Chunk<F32> (&v)[kMaxRpt], int n
     }
   }
   __syncthreads();
+  if constexpr (BW) {
+    const int nc = rows_here * D;
+    uint32_t* wd = reinterpret_cast<uint32_t*>(dst);
+    for (int k = lt; k < (nc + 9) / 10; k += gs) wd[k] = word_from_dense3(my_stage, k, nc);
+    return;
+  }
   const int nbytes = rows_here * R;
   const int head = min((16 - mis) & 15, nbytes);
   const int body = (nbytes - head) >> 4;
@@ -153,7 +163,7 @@ __device__ __forceinline__ void pack_store(const Chunk<F32> (&v)[kMaxRpt], int n
   if (lt < tail) dst[head + 16 * body + lt] = sp[head + 16 * body + lt];
 }
 
-template <int D, int BITS, bool F32, bool CHECK, bool STREAM>
+template <int D, int BITS, bool F32, bool CHECK, bool STREAM, bool BW>
 __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
   constexpr int CPR = D / 8;  // 8-channel chunks per row
   constexpr float LEVELS = (float)((1 << BITS) - 1);
@@ -272,7 +282,8 @@ __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
   }
 
   // ---- phase 4: codes, pack, stage, store ----------------------------------
-  uint8_t* dst_tile = p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R;
+  uint8_t* dst_tile = BW ? p.codes[kv] + ((int64_t)bh * p.bh_words + p.word_off) * 4
+                        : p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R;
   for (int pass = 0; pass < n_pass; ++pass) {
     const int pass_row0 = pass * rows_per_pass;
     const int row_base = pass_row0 + r0;
@@ -284,21 +295,24 @@ __global__ __launch_bounds__(kWG) void quant_pack_kernel(QuantParams p) {
         if (i < nvalid)
           load_chunk<F32>(v[i], src, base + (int64_t)(row_base + i * rps) * row_stride);
     }
-    uint8_t* dst = dst_tile + (int64_t)pass_row0 * p.R;
+    uint8_t* dst = BW ? dst_tile + 4 * ((int64_t)pass_row0 * D / 10) : dst_tile + (int64_t)pass_row0 * p.R;
     const int rows_here = max(0, min(n - pass_row0, rows_per_pass));
-    pack_store<D, BITS, F32>(v, nvalid, r0, rps, cg, zf, inv, my_stage, dst, rows_here, p.R, lt, gs);
+    pack_store<D, BITS, F32, BW>(v, nvalid, r0, rps, cg, zf, inv, my_stage, dst, rows_here, p.R, lt, gs);
     if constexpr (STREAM) __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Token-sliced path (few large tiles).  A slice is one register pass of a
-// 256-thread workgroup: kSliceRows(D) rows.  Slice s of a tile parks its 2 x D
-// float extremes at float offset 2 D s of the tile's block rows (n_k * R bytes,
-// at least 8 D bytes per slice for every supported width, checked by the host).
+// 256-thread workgroup: kSliceRows(D) rows (5 rows per thread for block-aligned
+// words, so that every slice starts on a word).  Slice s of a tile parks its
+// 2 x D float extremes at float offset 2 D s of the block's packed codes (at
+// least 8 D bytes per slice for every supported width, checked by the host).
 // ---------------------------------------------------------------------------
-template <int D>
-constexpr int kSliceRows = (kWG / (D / 8)) * kMaxRpt;
+template <bool BW>
+constexpr int kSliceRpt = BW ? 5 : kMaxRpt;
+template <int D, bool BW>
+constexpr int kSliceRows = (kWG / (D / 8)) * kSliceRpt<BW>;
 
 __device__ __forceinline__ void tile_of(const QuantParams& p, int64_t tile, int& kv, int& bh, int& b,
                                         int& h) {
@@ -309,24 +323,24 @@ __device__ __forceinline__ void tile_of(const QuantParams& p, int64_t tile, int&
 }
 
 // load this thread's rows of slice `slice` of a tile into registers
-template <int D, bool F32>
+template <int D, bool F32, bool BW>
 __device__ __forceinline__ int load_slice(const QuantParams& p, int kv, int b, int h, int slice,
                                           int tid, Chunk<F32> (&v)[kMaxRpt]) {
   constexpr int CPR = D / 8;
   constexpr int rps = kWG / CPR;
   const int cg = tid % CPR;
-  const int row_base = slice * kSliceRows<D> + tid / CPR;
+  const int row_base = slice * kSliceRows<D, BW> + tid / CPR;
   const int64_t row_stride = (int64_t)p.H * D;
   const int64_t base = ((int64_t)b * p.n * p.H + h) * D + 8 * cg;
   int nvalid = 0;
-  if (row_base < p.n) nvalid = min(kMaxRpt, (p.n - row_base + rps - 1) / rps);
+  if (row_base < p.n) nvalid = min(kSliceRpt<BW>, (p.n - row_base + rps - 1) / rps);
 #pragma unroll
   for (int i = 0; i < kMaxRpt; ++i)
     if (i < nvalid) load_chunk<F32>(v[i], p.src[kv], base + (int64_t)(row_base + i * rps) * row_stride);
   return nvalid;
 }
 
-template <int D, bool F32, bool CHECK>
+template <int D, bool F32, bool CHECK, bool BW>
 __global__ __launch_bounds__(kWG) void slice_extremes_kernel(QuantParams p, int n_slices) {
   constexpr int CPR = D / 8;
   __shared__ float red_mn[kWG / kWave][CPR][8];
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(kWG) void slice_extremes_kernel(QuantParams p, int 
   int kv, bh, b, h;
   tile_of(p, tile, kv, bh, b, h);
   Chunk<F32> v[kMaxRpt];
-  const int nvalid = load_slice<D, F32>(p, kv, b, h, slice, tid, v);
+  const int nvalid = load_slice<D, F32, BW>(p, kv, b, h, slice, tid, v);
   float mn[8], mx[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -364,8 +378,7 @@ __global__ __launch_bounds__(kWG) void slice_extremes_kernel(QuantParams p, int 
   }
   __syncthreads();
   if (tid < CPR) {
-    float* ext = reinterpret_cast<float*>(p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R) +
-                 (int64_t)slice * 2 * D;
+    float* ext = reinterpret_cast<float*>(block_codes(p, kv, bh)) + (int64_t)slice * 2 * D;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float lo = red_mn[0][tid][j], hi = red_mx[0][tid][j];
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(D) void slice_stats_kernel(QuantParams p, int n_sli
   const int ch = threadIdx.x;
   int kv, bh, b, h;
   tile_of(p, blockIdx.x, kv, bh, b, h);
-  const float* ext = reinterpret_cast<const float*>(p.codes[kv] + ((int64_t)bh * p.T + p.off) * p.R);
+  const float* ext = reinterpret_cast<const float*>(block_codes(p, kv, bh));
   float lo = __uint_as_float(0x7F800000u), hi = __uint_as_float(0xFF800000u);
 #pragma unroll 8
   for (int sl = 0; sl < n_slices; ++sl) {
@@ -412,7 +425,7 @@ __global__ __launch_bounds__(D) void slice_stats_kernel(QuantParams p, int n_sli
 
 // codes of one slice from the tile's binary16 statistics (zero and reciprocal
 // step rebuilt exactly as group_stats makes them)
-template <int D, int BITS, bool F32>
+template <int D, int BITS, bool F32, bool BW>
 __global__ __launch_bounds__(kWG) void slice_pack_kernel(QuantParams p, int n_slices) {
   constexpr int CPR = D / 8;
   __shared__ __align__(16) uint8_t stage[kStageBytes<BITS>];
@@ -422,7 +435,7 @@ __global__ __launch_bounds__(kWG) void slice_pack_kernel(QuantParams p, int n_sl
   int kv, bh, b, h;
   tile_of(p, tile, kv, bh, b, h);
   Chunk<F32> v[kMaxRpt];
-  const int nvalid = load_slice<D, F32>(p, kv, b, h, slice, tid, v);
+  const int nvalid = load_slice<D, F32, BW>(p, kv, b, h, slice, tid, v);
   const int cg = tid % CPR;
   const int64_t so = (((int64_t)b * p.H + h) * p.NB + p.block) * D + 8 * cg;
   const u32x4 zw = *reinterpret_cast<const u32x4*>(p.zero[kv] + so);
@@ -435,61 +448,64 @@ __global__ __launch_bounds__(kWG) void slice_pack_kernel(QuantParams p, int n_sl
     const float sf = h2f((uint16_t)((j & 1) ? (spair >> 16) : (spair & 0xFFFFu)));
     inv[j] = (sf > 0.0f) ? 1.0f / sf : 0.0f;
   }
-  const int row0 = slice * kSliceRows<D>;
-  uint8_t* dst = p.codes[kv] + ((int64_t)bh * p.T + p.off + row0) * p.R;
-  const int rows_here = min(p.n - row0, kSliceRows<D>);
-  pack_store<D, BITS, F32>(v, nvalid, tid / CPR, kWG / CPR, cg, zf, inv, stage, dst, rows_here, p.R,
-                           tid, kWG);
+  const int row0 = slice * kSliceRows<D, BW>;
+  uint8_t* dst = block_codes(p, kv, bh) + (BW ? 4 * ((int64_t)row0 * D / 10) : (int64_t)row0 * p.R);
+  const int rows_here = min(p.n - row0, kSliceRows<D, BW>);
+  pack_store<D, BITS, F32, BW>(v, nvalid, tid / CPR, kWG / CPR, cg, zf, inv, stage, dst, rows_here,
+                               p.R, tid, kWG);
 }
 
 // tiles below which a block too large for registers is cut into slices
 constexpr int64_t kSliceTiles = 1024;
 
-template <int D, int BITS, bool F32, bool CHECK>
+template <int D, int BITS, bool F32, bool CHECK, bool BW>
 hipError_t launch_sliced(const QuantParams& p, hipStream_t s) {
-  const int n_slices = (p.n + kSliceRows<D> - 1) / kSliceRows<D>;
-  // parked extremes must fit the block's rows
-  if ((int64_t)n_slices * 8 * D > (int64_t)p.n * p.R) return hipErrorInvalidValue;
+  const int n_slices = (p.n + kSliceRows<D, BW> - 1) / kSliceRows<D, BW>;
+  // parked extremes must fit the block's packed codes
+  const int64_t block_bytes = BW ? 4 * (((int64_t)p.n * D + 9) / 10) : (int64_t)p.n * p.R;
+  if ((int64_t)n_slices * 8 * D > block_bytes) return hipErrorInvalidValue;
   if (!dispatch_fits(p.n_tiles * n_slices, kWG)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(p.n_tiles * n_slices));
-  hipLaunchKernelGGL((slice_extremes_kernel<D, F32, CHECK>), grid, dim3(kWG), 0, s, p, n_slices);
+  hipLaunchKernelGGL((slice_extremes_kernel<D, F32, CHECK, BW>), grid, dim3(kWG), 0, s, p, n_slices);
   hipLaunchKernelGGL((slice_stats_kernel<D, BITS, F32, CHECK>), dim3((unsigned)p.n_tiles), dim3(D), 0,
                      s, p, n_slices);
-  hipLaunchKernelGGL((slice_pack_kernel<D, BITS, F32>), grid, dim3(kWG), 0, s, p, n_slices);
+  hipLaunchKernelGGL((slice_pack_kernel<D, BITS, F32, BW>), grid, dim3(kWG), 0, s, p, n_slices);
   return hipGetLastError();
 }
 
-template <int D, int BITS, bool F32>
+template <int D, int BITS, bool F32, bool BW>
 hipError_t launch_t(const QuantParams& p, hipStream_t s) {
   const int tiles_per_wg = kWG / p.gs;
   const int64_t grid = (p.n_tiles + tiles_per_wg - 1) / tiles_per_wg;
   const bool stream = (int64_t)(p.gs / (D / 8)) * p.rpt < p.n;
   const bool check = p.status != nullptr;
   if (stream && p.n_tiles < kSliceTiles)
-    return check ? launch_sliced<D, BITS, F32, true>(p, s) : launch_sliced<D, BITS, F32, false>(p, s);
+    return check ? launch_sliced<D, BITS, F32, true, BW>(p, s)
+                 : launch_sliced<D, BITS, F32, false, BW>(p, s);
   if (!dispatch_fits(grid, kWG)) return hipErrorInvalidConfiguration;
   dim3 g((unsigned)grid), blk(kWG);
   if (check) {
     if (stream)
-      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, true, true>), g, blk, 0, s, p);
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, true, true, BW>), g, blk, 0, s, p);
     else
-      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, true, false>), g, blk, 0, s, p);
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, true, false, BW>), g, blk, 0, s, p);
   } else {
     if (stream)
-      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, false, true>), g, blk, 0, s, p);
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, false, true, BW>), g, blk, 0, s, p);
     else
-      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, false, false>), g, blk, 0, s, p);
+      hipLaunchKernelGGL((quant_pack_kernel<D, BITS, F32, false, false, BW>), g, blk, 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool BW = false>
 hipError_t launch_b(const QuantParams& p, bool f32src, hipStream_t s) {
-  return f32src ? launch_t<D, BITS, true>(p, s) : launch_t<D, BITS, false>(p, s);
+  return f32src ? launch_t<D, BITS, true, BW>(p, s) : launch_t<D, BITS, false, BW>(p, s);
 }
 
 template <int D>
 hipError_t launch_d(const QuantParams& p, int bits, bool f32src, hipStream_t s) {
+  if (p.word_layout) return bits == 3 ? launch_b<D, 3, true>(p, f32src, s) : hipErrorInvalidValue;
   switch (bits) {
     case 2: return launch_b<D, 2>(p, f32src, s);
     case 3: return launch_b<D, 3>(p, f32src, s);

@@ -157,9 +157,14 @@ def kvq_bytes(layout: Layout, n_filled: int) -> Tuple[int, int]:
 
 
 def cache_shapes(layout: Layout) -> Dict[str, Tuple[int, ...]]:
+    """pack_mode 0: codes [B][H][T][R] bytes; pack_mode 2: [B][H][4 W] bytes, the
+    W 32-bit words of every block's stream (kvq_bytes gives B*H*4*W)."""
     B, H, D, NB = layout.batch, layout.heads, layout.head_dim, layout.n_blocks
-    return {"codes": (B, H, layout.total_tokens, layout.row_bytes), "zero": (B, H, NB, D),
-            "scale": (B, H, NB, D)}
+    if layout.pack_mode == 2:
+        codes = (B, H, kvq_bytes(layout, NB)[0] // (B * H))
+    else:
+        codes = (B, H, layout.total_tokens, layout.row_bytes)
+    return {"codes": codes, "zero": (B, H, NB, D), "scale": (B, H, NB, D)}
 
 
 def alloc_cache(layout: Layout, device="cuda") -> Dict[str, torch.Tensor]:
