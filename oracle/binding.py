@@ -13,7 +13,8 @@ from typing import Dict, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# KVQR_ORACLE_LIB names another build of the same source (the sanitizer build)
+LIB_PATH = os.environ.get("KVQR_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 MAX_BLOCKS = 64
 OK, E_INVAL = 0, -1

@@ -13,18 +13,25 @@ LIB = os.path.join(HERE, "liboracle.so")
 SOURCES = [os.path.join(HERE, "kvq_oracle.c")]
 
 
-def build(verbose: bool = False) -> str:
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False, cc: str = "gcc") -> str:
+    """sanitize: AddressSanitizer + UndefinedBehaviorSanitizer instrumentation
+    (any finding aborts); load the result with the sanitizer runtime of the
+    compiler `cc` preloaded."""
     cmd = [
-        "gcc", "-std=c11", "-O2", "-fPIC", "-shared",
+        cc, "-std=c11", "-O1" if sanitize else "-O2", "-fPIC", "-shared",
         "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
-        "-Wall", "-Wextra", "-Werror",
-        "-o", LIB + ".tmp", *SOURCES, "-lm",
+        "-Wall", "-Wextra", "-Werror", *(SAN_FLAGS if sanitize else []),
+        "-o", out + ".tmp", *SOURCES, "-lm",
     ]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -31,9 +31,20 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizer build (libkvq_san.so): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the C ABI's host code (kvq_api.hip: argument
+# validation, layout arithmetic, descriptors), linked with the ordinary objects
+# of the kernel sources.  Loaded with clang's ASan runtime preloaded, by CPU
+# tests that never launch a kernel.
+SAN_LIB = os.path.join(PKG, "libkvq_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    obj = os.path.join(BUILD, src.replace(".hip", "_san.o" if sanitize else ".o"))
+    cmd = [HIPCC, *CFLAGS, *(SAN_FLAGS if sanitize else []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,18 +53,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False, out: str = "") -> str:
+    out = out or (SAN_LIB if sanitize else LIB)
     os.makedirs(BUILD, exist_ok=True)
+
+    def one(src):
+        if sanitize and src != "kvq_api.hip":
+            obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+            return obj if os.path.exists(obj) else _compile(src, verbose)
+        return _compile(src, verbose, sanitize)
+
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        objs = list(ex.map(one, SOURCES))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -15,7 +15,8 @@ from typing import Dict, Optional, Sequence, Tuple
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libkvq.so")
+# KVQ_LIB names another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(PKG, "libkvq.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "kvq.h")
 
 MAX_BLOCKS = 64
