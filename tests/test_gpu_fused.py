@@ -50,8 +50,17 @@ def decode_both_ways(oracle, wl, layer=0, scale=0.0):
     vi.Workload("int2", 1, 2, 3, 64, 2, vi.VAR_BLOCKS, "bf16", seed=41),
     vi.Workload("int8_rope", 1, 2, 3, 64, 8, (1, 7, 32, 33, 100, 256), "bf16", rope=True, seed=43),
     vi.Workload("int8_f32", 1, 2, 3, 64, 8, (1, 4, 9, 16, 25), "f32", seed=47),
+    # head_dim 128 through the workgroup fused kernels (2, 4 and 8 waves; a
+    # 2-wave workgroup takes 4 lanes per 8-channel chunk, the others 8 lanes
+    # and two waves per row), every width, ragged blocks up to 256 tokens
+    vi.Workload("d128_int4", 1, 2, 3, 128, 4, (1, 33, 64, 65, 100, 128, 129, 256), "bf16",
+                seed=101),
+    vi.Workload("d128_int3_rope", 1, 2, 3, 128, 3, vi.VAR_BLOCKS, "bf16", rope=True, seed=103),
+    vi.Workload("d128_int2", 1, 2, 3, 128, 2, (7, 40, 97, 200), "bf16", seed=107),
+    vi.Workload("d128_int8", 1, 2, 3, 128, 8, (7, 40, 97, 200), "bf16", seed=109),
 ], ids=["tiny_f32", "d20_int4", "d20_int3_rope", "d24_int4", "edge_int3", "edge_d128",
-        "many_blocks", "int2", "int8_rope", "int8_f32"])
+        "many_blocks", "int2", "int8_rope", "int8_f32", "d128_int4", "d128_int3_rope",
+        "d128_int2", "d128_int8"])
 def test_fused_matches_two_calls_and_oracle(oracle, wl):
     kf, vf, ks, vs, ko, vo, steps = decode_both_ways(oracle, wl)
     assert_cache_equal(kf, ko, "fused K")
@@ -112,11 +121,13 @@ def test_fused_full_batch_every_block(oracle):
     assert_cache_equal(vf, vo, "fused V")
 
 
-@pytest.mark.parametrize("src,second", [("bf16", 16), ("f32", 16), ("bf16", 64), ("bf16", 200)])
-def test_fused_status_flags(oracle, src, second):
+@pytest.mark.parametrize("src,second,head_dim", [("bf16", 16, 64), ("f32", 16, 64),
+                                                 ("bf16", 64, 64), ("bf16", 200, 64),
+                                                 ("bf16", 64, 128), ("bf16", 200, 128)])
+def test_fused_status_flags(oracle, src, second, head_dim):
     """Input screening through the fused call: the one-wave path (16 tokens) and
-    the workgroup path (64 and 200 tokens)."""
-    wl = vi.Workload("status", 1, 2, 3, 64, 4, (16, second), src, seed=5)
+    the workgroup path (64 and 200 tokens, head_dim 64 and 128)."""
+    wl = vi.Workload("status", 1, 2, 3, head_dim, 4, (16, second), src, seed=5)
     Lg, _ = layouts(oracle, wl)
     k0, v0 = vi.kv_block(wl, 0, "k", 0), vi.kv_block(wl, 0, "v", 0)
     kb, vb = vi.kv_block(wl, 0, "k", 1), vi.kv_block(wl, 0, "v", 1)

@@ -161,12 +161,13 @@ def test_split_ranges_equal_dense_rows(oracle):
     vi.WORKLOADS["var_d20_b128_int3_rope"].with_(batch=2),
     vi.Workload("edge", 1, 1, 3, 64, 3, (1, 7, 32, 33, 2, 256, 3), "bf16", rope=True, seed=83),
     vi.Workload("f32", 1, 2, 3, 64, 3, (1, 4, 9, 16, 25), "f32", seed=89),
-    vi.Workload("d128", 1, 2, 3, 128, 3, (5, 31, 40), "bf16", seed=97),
-], ids=["d20", "edge", "f32_short", "d128_two_calls"])
+    vi.Workload("d128", 1, 2, 3, 128, 3, (5, 31, 40, 97, 256), "bf16", seed=97),
+], ids=["d20", "edge", "f32_short", "d128"])
 def test_fused_equals_two_calls_and_oracle(oracle, wl):
     """kvq_quantize_attend over the word layout (the one-wave and workgroup
-    fused kernels; two launches where none covers the shape): the cache is the
-    oracle's and the outputs are those of the two calls, bit for bit."""
+    fused kernels at head_dim 64 and 128; two launches where none covers the
+    shape): the cache is the oracle's and the outputs are those of the two
+    calls, bit for bit."""
     Lg, Lo = layouts(oracle, wl, 2)
     kf, vf = K.alloc_cache(Lg), K.alloc_cache(Lg)
     ks, vs = K.alloc_cache(Lg), K.alloc_cache(Lg)

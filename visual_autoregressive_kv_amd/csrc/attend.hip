@@ -192,37 +192,65 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* prefi
 // Fused launch, quantize side for a workgroup that owns one (sequence, head):
 // the first half of the threads quantizes block k of K, the second half of V
 // (bf16 input, the same group statistics and code arithmetic as the standalone
-// quantize kernel).  Lane l of a wave holds chunk c = l / 8 (channels 8 c ..
-// 8 c + 7) of rows rg, rg + RG, .. (at most 8) with rg = 8 w + l % 8 for the
-// half's wave w, so the 8 lanes sharing a chunk are neighbours:
+// quantize kernel).  Within a wave, L neighbouring lanes share one 8-channel
+// chunk (L = 8, or 4 for a 2-wave workgroup at head_dim 128), so a wave covers
+// 64 / L chunks and CW = D / 8 / (64 / L) waves cover a row; lane l of the
+// half's wave w holds chunk (w % CW) * 64 / L + l / L of rows rl, rl + RG, ..
+// (at most MAXR) with row lane rl = (w / CW) * L + l % L:
 //   - per thread: v_min3 / v_max3 over row pairs (for the odd bf16 channel of
 //     a word the raw word is the ordering key, masked afterwards);
-//   - across the 8 lanes of a chunk: three DPP steps (xor 1, xor 2 inside a
-//     quad, then the mirror of the half-row);
-//   - across the half's waves: LDS; one wave per half then computes every
-//     channel's statistics once (lane = channel);
+//   - across the L lanes of a chunk: DPP steps (xor 1, xor 2 inside a quad,
+//     then for L = 8 the mirror of the half-row);
+//   - across the half's row waves: LDS; the half's first D threads then compute
+//     every channel's statistics once (thread = channel);
 //   - codes: every thread packs its rows into an LDS copy of the block's rows
 //     (with the destination's 16-byte misalignment), which the half writes to
 //     the cache with 128-bit stores plus byte-exact head and tail.
 // The packed rows reach the cache before the caller's barrier, so the attention
 // reads them back like older blocks.
-// scratch: (NW + 2) * 2 * 64 floats; stage_k, stage_v: 16 + 32 * NW * R bytes each.
+// scratch: wg_quant_scratch<D, NW>() floats; stage_k, stage_v: 16 + 32 * NW * R bytes each.
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// lanes sharing a chunk, chunks per wave, waves per row, row lanes, rows per thread
+template <int D, int NW>
+struct WgQuantShape {
+  static constexpr int CPR = D / 8;
+  static constexpr int WT = NW / 2;                         // waves per tensor
+  static constexpr int L = (D == 128 && NW == 2) ? 4 : 8;   // lanes per chunk in a wave
+  static constexpr int CPW = kWave / L;                     // chunks per wave
+  static constexpr int CW = CPR / CPW;                      // waves per row
+  static constexpr int RW = WT / CW;                        // row waves
+  static constexpr int RG = RW * L;                         // row lanes per tensor
+  static constexpr int MAXR = (NW * 32 + RG - 1) / RG;      // rows per thread (n <= NW * 32)
+  static_assert(CPR % CPW == 0 && WT % CW == 0 && RW >= 1, "chunk layout must tile the row");
+};
+// scratch floats of quantize_block_wg: per tensor and row wave the channel
+// extremes, then per tensor the channel zero points and reciprocal steps (no
+// prologue below 2 waves)
+template <int D, int NW>
+__host__ __device__ constexpr int wg_quant_scratch() {
+  if constexpr (NW < 2) {
+    return 0;
+  } else {
+    return 2 * WgQuantShape<D, NW>::RW * 2 * D + 2 * 2 * D;
+  }
+}
+
 template <int D, int BITS, int NW, bool CHECK, bool BW>
 __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, int h, int tid,
                                                   _Float16* st_lds, float* scratch,
                                                   uint8_t* stage_k, uint8_t* stage_v, int& vover) {
-  static_assert(D == kWave && NW >= 2, "64-channel heads, at least one wave per tensor");
+  using S = WgQuantShape<D, NW>;
+  static_assert((D == 64 || D == 128) && NW >= 2, "64- or 128-channel heads, a wave per tensor");
   constexpr int CPR = D / 8;
   constexpr int GT = NW * kWave / 2;  // threads per tensor
-  constexpr int WT = NW / 2;          // waves per tensor
-  constexpr int RG = GT / CPR;        // row groups, 8 per wave
-  constexpr int MAXR = 8;             // rows per thread (n <= RG * MAXR)
+  constexpr int L = S::L;
+  constexpr int RG = S::RG;
+  constexpr int MAXR = S::MAXR;
   constexpr float LEVELS = (float)((1 << BITS) - 1);
   const FuseParams& f = p.fz;
   const int n = p.n;
@@ -230,8 +258,9 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
   const int tensor = tid / GT;
   const int u = tid % GT;
   const int wt = u / kWave;
-  const int c = lane >> 3;
-  const int rg = wt * 8 + (lane & 7);
+  const int c = (wt % S::CW) * S::CPW + lane / L;
+  const int rw = wt / S::CW;  // row wave
+  const int rg = rw * L + lane % L;
   const int64_t row_stride = (int64_t)p.H * D;
   const int64_t base = ((int64_t)b * n * p.H + h) * D + 8 * c;
   const uint16_t* src = static_cast<const uint16_t*>(f.src[tensor]);
@@ -277,22 +306,24 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
       }
     }
   }
-  // the 8 lanes holding chunk c: xor 1 and xor 2 inside each quad, then the
-  // mirror of each half-row (lane i with lane 7 - i)
+  // the L lanes holding chunk c: xor 1 and xor 2 inside each quad, then for
+  // L = 8 the mirror of each half-row (lane i with lane 7 - i)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     mn[j] = min3f(mn[j], dpp_f32<0xB1>(mn[j]), mn[j]);
     mx[j] = max3f(mx[j], dpp_f32<0xB1>(mx[j]), mx[j]);
     mn[j] = min3f(mn[j], dpp_f32<0x4E>(mn[j]), mn[j]);
     mx[j] = max3f(mx[j], dpp_f32<0x4E>(mx[j]), mx[j]);
-    mn[j] = min3f(mn[j], dpp_f32<0x141>(mn[j]), mn[j]);
-    mx[j] = max3f(mx[j], dpp_f32<0x141>(mx[j]), mx[j]);
+    if constexpr (L == 8) {
+      mn[j] = min3f(mn[j], dpp_f32<0x141>(mn[j]), mn[j]);
+      mx[j] = max3f(mx[j], dpp_f32<0x141>(mx[j]), mx[j]);
+    }
   }
-  float* red = scratch;                          // [tensor][wave][min|max][64]
-  float* zi = scratch + 2 * WT * 2 * kWave;      // [tensor][zero|reciprocal][64]
-  if ((lane & 7) == 0) {
-    float* rm = red + ((tensor * WT + wt) * 2 + 0) * kWave + 8 * c;
-    float* rx = red + ((tensor * WT + wt) * 2 + 1) * kWave + 8 * c;
+  float* red = scratch;                          // [tensor][row wave][min|max][D]
+  float* zi = scratch + 2 * S::RW * 2 * D;       // [tensor][zero|reciprocal][D]
+  if (lane % L == 0) {
+    float* rm = red + ((tensor * S::RW + rw) * 2 + 0) * D + 8 * c;
+    float* rx = red + ((tensor * S::RW + rw) * 2 + 1) * D + 8 * c;
     *reinterpret_cast<f32x4*>(rm) = f32x4{mn[0], mn[1], mn[2], mn[3]};
     *reinterpret_cast<f32x4*>(rm + 4) = f32x4{mn[4], mn[5], mn[6], mn[7]};
     *reinterpret_cast<f32x4*>(rx) = f32x4{mx[0], mx[1], mx[2], mx[3]};
@@ -300,14 +331,15 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
   }
   __syncthreads();
   int flags = 0;
-  if (u < kWave) {  // first wave of each half: lane = channel
-    const int ch = lane;
-    float lo = red[((tensor * WT) * 2 + 0) * kWave + ch];
-    float hi = red[((tensor * WT) * 2 + 1) * kWave + ch];
+  // the half's threads take one channel each (two for a 2-wave workgroup at
+  // head_dim 128)
+  for (int ch = u; ch < D; ch += GT) {
+    float lo = red[((tensor * S::RW) * 2 + 0) * D + ch];
+    float hi = red[((tensor * S::RW) * 2 + 1) * D + ch];
 #pragma unroll
-    for (int wv = 1; wv < WT; ++wv) {
-      lo = min3f(lo, red[((tensor * WT + wv) * 2 + 0) * kWave + ch], lo);
-      hi = max3f(hi, red[((tensor * WT + wv) * 2 + 1) * kWave + ch], hi);
+    for (int wv = 1; wv < S::RW; ++wv) {
+      lo = min3f(lo, red[((tensor * S::RW + wv) * 2 + 0) * D + ch], lo);
+      hi = max3f(hi, red[((tensor * S::RW + wv) * 2 + 1) * D + ch], hi);
     }
     if (ch & 1) {  // the raw-word keys of odd channels
       lo = __uint_as_float(__float_as_uint(lo) & 0xFFFF0000u);
@@ -320,16 +352,16 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     _Float16* srow = st_lds + ((f.block * 2 + tensor) * 2) * D;
     srow[ch] = __builtin_bit_cast(_Float16, gst.zb);
     srow[D + ch] = __builtin_bit_cast(_Float16, gst.sb);
-    zi[(tensor * 2 + 0) * kWave + ch] = gst.zf;
-    zi[(tensor * 2 + 1) * kWave + ch] = gst.inv;
+    zi[(tensor * 2 + 0) * D + ch] = gst.zf;
+    zi[(tensor * 2 + 1) * D + ch] = gst.inv;
     if (tensor == 1) vover |= __builtin_fmaf(LEVELS, h2f(gst.sb), gst.zf) > 65504.0f;
   }
   __syncthreads();
   float zf[8], inv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    zf[j] = zi[(tensor * 2 + 0) * kWave + 8 * c + j];
-    inv[j] = zi[(tensor * 2 + 1) * kWave + 8 * c + j];
+    zf[j] = zi[(tensor * 2 + 0) * D + 8 * c + j];
+    inv[j] = zi[(tensor * 2 + 1) * D + 8 * c + j];
   }
   uint8_t* dst = BW ? f.codes[tensor] + (((int64_t)b * p.H + h) * p.bh_words + f.word_off) * 4
                     : f.codes[tensor] + (((int64_t)b * p.H + h) * p.T_cache + f.off) * p.R;
@@ -416,7 +448,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_
   // fused prologue: block rows staged in k_lo (K) and v_t (V), extremes in k_hi
   static_assert(FUSE == 0 || ((BITS != 3 || (sizeof(k_lo) >= 16 + NW * 32 * BITS * D / 8 &&
                                              sizeof(v_t) >= 16 + NW * 32 * BITS * D / 8)) &&
-                              sizeof(k_hi) >= (NW + 2) * 2 * kWave * sizeof(float)),
+                              sizeof(k_hi) >= wg_quant_scratch<D, NW>() * sizeof(float)),
                 "LDS too small for the quantize prologue");
   const int wg = SPLIT ? (int)(blockIdx.x / p.splits) : (int)blockIdx.x;
   const int sp = SPLIT ? (int)blockIdx.x - wg * p.splits : 0;
@@ -1431,13 +1463,20 @@ static void fill_fuse(AttendParams& p, const QuantParams& q) {
   p.fz.word_off = q.word_off;
 }
 
-template <int BITS, bool BW = false>
-static hipError_t launch_wg_fused(const AttendParams& p, int waves, bool check, hipStream_t s) {
+template <int D, int BITS, bool BW = false>
+static hipError_t launch_wg_fused_d(const AttendParams& p, int waves, bool check, hipStream_t s) {
   if (waves <= 2)
-    return check ? launch_nw<64, BITS, 2, 2, 0, BW>(p, s) : launch_nw<64, BITS, 2, 1, 0, BW>(p, s);
+    return check ? launch_nw<D, BITS, 2, 2, 0, BW>(p, s) : launch_nw<D, BITS, 2, 1, 0, BW>(p, s);
   if (waves <= 4)
-    return check ? launch_nw<64, BITS, 4, 2, 0, BW>(p, s) : launch_nw<64, BITS, 4, 1, 0, BW>(p, s);
-  return check ? launch_nw<64, BITS, 8, 2, 0, BW>(p, s) : launch_nw<64, BITS, 8, 1, 0, BW>(p, s);
+    return check ? launch_nw<D, BITS, 4, 2, 0, BW>(p, s) : launch_nw<D, BITS, 4, 1, 0, BW>(p, s);
+  return check ? launch_nw<D, BITS, 8, 2, 0, BW>(p, s) : launch_nw<D, BITS, 8, 1, 0, BW>(p, s);
+}
+
+template <int BITS, bool BW = false>
+static hipError_t launch_wg_fused(const AttendParams& p, int head_dim, int waves, bool check,
+                                  hipStream_t s) {
+  return head_dim == 64 ? launch_wg_fused_d<64, BITS, BW>(p, waves, check, s)
+                        : launch_wg_fused_d<128, BITS, BW>(p, waves, check, s);
 }
 
 hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, int head_dim,
@@ -1459,17 +1498,18 @@ hipError_t launch_quantize_attend(const QuantParams& q, const AttendParams& a, i
   }
   // larger blocks: the workgroup kernels with one query tile per (sequence, head)
   const int waves = (a.n + 31) / 32;
-  if (head_dim == 64 && !f32src && a.n <= kMaxWaves * 32 && waves >= 2) {
+  if ((head_dim == 64 || head_dim == 128) && !f32src && a.n <= kMaxWaves * 32 && waves >= 2) {
     AttendParams p = a;
     fill_fuse(p, q);
     const bool check = q.status != nullptr;
     if (a.word_layout)
-      return bits == 3 ? launch_wg_fused<3, true>(p, waves, check, s) : hipErrorInvalidValue;
+      return bits == 3 ? launch_wg_fused<3, true>(p, head_dim, waves, check, s)
+                       : hipErrorInvalidValue;
     switch (bits) {
-      case 2: return launch_wg_fused<2>(p, waves, check, s);
-      case 3: return launch_wg_fused<3>(p, waves, check, s);
-      case 4: return launch_wg_fused<4>(p, waves, check, s);
-      case 8: return launch_wg_fused<8>(p, waves, check, s);
+      case 2: return launch_wg_fused<2>(p, head_dim, waves, check, s);
+      case 3: return launch_wg_fused<3>(p, head_dim, waves, check, s);
+      case 4: return launch_wg_fused<4>(p, head_dim, waves, check, s);
+      case 8: return launch_wg_fused<8>(p, head_dim, waves, check, s);
       default: return hipErrorInvalidValue;
     }
   }
