@@ -65,6 +65,8 @@ def parse():
                     help="quantize and attend with separate calls for every block")
     ap.add_argument("--no-split", action="store_true",
                     help="attend with kvq_attend_packed instead of kvq_attend_packed_split")
+    ap.add_argument("--pack-mode", type=int, default=0, choices=(0, 2),
+                    help="cache layout: 0 dense rows, 2 block-aligned 32-bit words")
     ap.add_argument("--layers", type=int, default=0,
                     help="run this many of the workload's layers (0: all); for shapes whose "
                          "inputs for every layer do not fit in HBM at once")
@@ -75,20 +77,32 @@ def parse():
 # algorithmic bytes / flops (per launch)
 # ---------------------------------------------------------------------------
 
+PACK_MODE = 0  # cache layout of the run (--pack-mode)
+
+
+def block_code_bytes(wl, k: int) -> int:
+    """Packed codes of block k in one (sequence, head) cache: dense rows of
+    ceil(b D / 8) bytes, or (block-aligned words) ceil(n_k D / floor(32 / b))
+    32-bit words."""
+    n, D = wl.blocks[k], wl.head_dim
+    if PACK_MODE == 2:
+        cpw = 32 // wl.bits
+        return 4 * ((n * D + cpw - 1) // cpw)
+    return n * ((wl.bits * D + 7) // 8)
+
+
 def quant_bytes(wl, k: int) -> int:
-    """Read the block's K and V once, write their packed rows and statistics."""
+    """Read the block's K and V once, write their packed codes and statistics."""
     B, H, D, n = wl.batch, wl.heads, wl.head_dim, wl.blocks[k]
-    R = (wl.bits * D + 7) // 8
     src = 2 if wl.src == "bf16" else 4
-    return 2 * (B * n * H * D * src + B * H * n * R + B * H * D * 4)
+    return 2 * (B * n * H * D * src + B * H * block_code_bytes(wl, k) + B * H * D * 4)
 
 
 def attend_bytes(wl, k: int) -> int:
     """Packed K/V prefix + their stats once per (sequence, head), Q in, O out (fp32)."""
     B, H, D, n = wl.batch, wl.heads, wl.head_dim, wl.blocks[k]
-    R = (wl.bits * D + 7) // 8
-    T = wl.offset(k) + n
-    return B * H * (2 * T * R + 2 * (k + 1) * D * 4 + n * D * 2 + n * D * 4)
+    prefix = sum(block_code_bytes(wl, j) for j in range(k + 1))
+    return B * H * (2 * prefix + 2 * (k + 1) * D * 4 + n * D * 2 + n * D * 4)
 
 
 def attend_flops(wl, k: int) -> int:
@@ -209,7 +223,9 @@ def cpu_baseline(wl, target_s: float):
 # ---------------------------------------------------------------------------
 
 def main():
+    global PACK_MODE
     args = parse()
+    PACK_MODE = args.pack_mode
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the packed-KV path runs on a single MI355X "
               "(it would shard across GPUs by batch or heads with no exchange; that "
@@ -228,7 +244,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = K.lib()
-    L = K.make_layout(wl.batch, wl.heads, wl.head_dim, wl.bits, wl.blocks)
+    L = K.make_layout(wl.batch, wl.heads, wl.head_dim, wl.bits, wl.blocks, PACK_MODE)
     NB = len(wl.blocks)
     print(f"[bench] {wl.name}: {wl.layers} layers, batch {wl.batch}, {wl.heads}x{wl.head_dim}, "
           f"INT{wl.bits}, {NB} blocks ({wl.total_tokens} tokens); drawing inputs", flush=True)
@@ -409,7 +425,7 @@ def main():
     dk = kinds[dominant]
     avg_bytes, avg_ms = dk["bytes"] / dk["launches"], dk["ms"] / dk["launches"]
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(dominant, wl.name)
+    traffic = measured_traffic(dominant, wl.name if PACK_MODE == 0 else f"{wl.name}_pm{PACK_MODE}")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "kernel": dominant,
@@ -472,6 +488,7 @@ def main():
         "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch,
                    "heads": wl.heads, "head_dim": wl.head_dim, "bits": wl.bits,
                    "schedule": list(wl.blocks), "tokens_per_seq": wl.total_tokens,
+                   "pack_mode": PACK_MODE,
                    "parallelism": "none (1 GPU)"},
         "kernels": kind_stats,
         "passes": passes,

@@ -37,6 +37,26 @@ def test_byte_model_against_the_cache_accounting(oracle):
         assert bench.attend_flops(wl, k) == 4 * B * H * n * (wl.offset(k) + n) * D
 
 
+def test_byte_model_of_block_aligned_words(oracle):
+    """--pack-mode 2: the attention reads the prefix's words (kvqr_bytes of the
+    block-aligned layout) and the quantizer writes the block's words."""
+    wl = vi.WORKLOADS["var_d20_b128_int3_rope"]
+    L = oracle.layout_of(wl)
+    L.pack_mode = 2
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    try:
+        bench.PACK_MODE = 2
+        for k in range(len(wl.blocks)):
+            code_b, _ = oracle.nbytes(L, k + 1)
+            prev_b, _ = oracle.nbytes(L, k)
+            n = wl.blocks[k]
+            assert bench.attend_bytes(wl, k) == 2 * code_b + B * H * (2 * (k + 1) * D * 4 +
+                                                                      n * D * (2 + 4))
+            assert bench.quant_bytes(wl, k) == 2 * (B * H * (n * D * 2 + D * 4) + code_b - prev_b)
+    finally:
+        bench.PACK_MODE = 0
+
+
 def test_per_layer_totals_quoted_in_the_docs():
     """VAR-d20 B128 INT4: 570.2 MB quantize+pack, 1020.7 MB attention and 187.7
     GFLOP per layer over the 10 blocks."""
