@@ -65,6 +65,9 @@ def parse():
                     help="quantize and attend with separate calls for every block")
     ap.add_argument("--no-split", action="store_true",
                     help="attend with kvq_attend_packed instead of kvq_attend_packed_split")
+    ap.add_argument("--roctx", action="store_true",
+                    help="mark every timed step and every (block, layer) call with roctx ranges "
+                         "(for rocprofv3 --marker-trace; adds host work to the timed loop)")
     ap.add_argument("--pack-mode", type=int, default=0, choices=(0, 2),
                     help="cache layout: 0 dense rows, 2 block-aligned 32-bit words")
     ap.add_argument("--layers", type=int, default=0,
@@ -308,10 +311,15 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     ws_ptr, ws_n = ws.data_ptr(), C.c_uint64(ws.numel())
 
+    call_labels = {}  # id(calls) -> one roctx label per call
+
     def build_calls(fuse: bool):
         calls = []  # (kind, block, function, arguments), in launch order
+        labs = []
         for j in range(NB):
             for l in range(wl.layers):
+                labs.extend([f"block {j + 1} layer {l}".encode()] *
+                            (1 if fuse and can_fuse(j) else 2))
                 # shapes are fixed by construction; checked once here
                 assert tuple(Kin[l][j].shape) == (wl.batch, wl.blocks[j], wl.heads, wl.head_dim)
                 if fuse and can_fuse(j):
@@ -331,6 +339,7 @@ def main():
                     calls.append(("attend", j, lib.kvq_attend_packed,
                                   (Lref, j, Qin[l][j].data_ptr(), kC[l], vC[l], C.c_float(0.0),
                                    Out[l][j].data_ptr(), sh)))
+        call_labels[id(calls)] = labs
         return calls
 
     calls = build_calls(fuse=not args.unfused)
@@ -339,16 +348,33 @@ def main():
     K.kvq_attend_packed(L, 0, Qin[0][0], kcs[0], vcs[0], Out[0][0])
     K.kvq_quantize_attend(L, 0, Kin[0][0], Vin[0][0], Qin[0][0], kcs[0], vcs[0], Out[0][0])
 
-    def step(cs, events=None):
+    # roctx ranges (--roctx): one per timed step, one per (block, layer) call
+    roctx = None
+    if args.roctx:
+        roctx = C.CDLL("libroctx64.so")
+        roctx.roctxRangePushA.argtypes = [C.c_char_p]
+        roctx.roctxRangePushA.restype = C.c_int
+        roctx.roctxRangePop.restype = C.c_int
+
+    def step(cs, events=None, mark=None):
         """One decode step; events[c] before call c and events[c + 1] after it."""
+        if mark is not None:
+            roctx.roctxRangePushA(mark)
         if events is not None:
             events[0].record(stream)
+        names = call_labels[id(cs)] if mark is not None else None
         for c, (_, _, fn, cargs) in enumerate(cs):
+            if names is not None:
+                roctx.roctxRangePushA(names[c])
             rc = fn(*cargs)
+            if names is not None:
+                roctx.roctxRangePop()
             if events is not None:
                 events[c + 1].record(stream)
             if rc:
                 raise RuntimeError(f"kvq launch failed (rc={rc}) at call {c}")
+        if mark is not None:
+            roctx.roctxRangePop()
 
     for w in range(args.warmup):
         step(calls)
@@ -369,12 +395,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):
+        mark = f"kvq step {s_}".encode() if roctx is not None else None
         if single_kind:
             evs[s_][0].record(stream)
-            step(calls)
+            step(calls, mark=mark)
             evs[s_][1].record(stream)
         else:
-            step(calls, evs[s_])
+            step(calls, evs[s_], mark=mark)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 

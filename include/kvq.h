@@ -62,6 +62,14 @@ extern "C" {
 
 #define KVQ_MAX_BLOCKS 64
 
+/*
+ * Debug mode: with KVQ_DEBUG=1 (any value but empty or "0") in the environment,
+ * every call that launches work synchronizes its stream after the launch
+ * (unless the stream is being captured into a graph) and checks
+ * hipGetLastError; a failure is printed on stderr with the call's name and
+ * returned as KVQ_E_DEVICE.  Off by default: calls are asynchronous.
+ */
+
 /* return codes */
 #define KVQ_OK 0
 #define KVQ_E_INVAL (-1)       /* bad argument, layout, pointer or alignment */

@@ -6,6 +6,8 @@ ranges).  Per case, block by block:
     kvq_attend_packed, and both caches are bit-exact against the oracle's;
   * two of the blocks' outputs are within the attention tolerance of the
     binary64 oracle, and so is kvq_attend_packed_split on the last block.
+A second sweep runs INT3 layouts in block-aligned words (pack_mode 2), whose
+kernels address each chunk per tile from its key's block.
 Sizes keep the oracle to a few seconds per case."""
 import numpy as np
 import pytest
@@ -18,6 +20,7 @@ from gpu_common import DEV, assert_cache_equal, check_attn, layouts, to_dev
 pytestmark = pytest.mark.gpu
 
 N_CASES = 48
+N_WORD_CASES = 24
 
 
 def random_workload(i: int) -> vi.Workload:
@@ -46,15 +49,23 @@ def random_workload(i: int) -> vi.Workload:
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_layout(oracle, i):
-    wl = random_workload(i)
-    Lg, Lo = layouts(oracle, wl)
+    run_case(oracle, random_workload(i), i, 0)
+
+
+@pytest.mark.parametrize("i", range(N_WORD_CASES))
+def test_random_layout_block_words(oracle, i):
+    run_case(oracle, random_workload(N_CASES + i).with_(bits=3), N_CASES + i, 2)
+
+
+def run_case(oracle, wl, i, pack_mode):
+    Lg, Lo = layouts(oracle, wl, pack_mode)
     kf, vf = K.alloc_cache(Lg), K.alloc_cache(Lg)
     ks, vs = K.alloc_cache(Lg), K.alloc_cache(Lg)
     ko, vo = oracle.alloc_cache(Lo), oracle.alloc_cache(Lo)
     nb = len(wl.blocks)
     checked = {nb - 1, int(np.random.default_rng(i).integers(nb))}
     print(f"[sweep] case {i}: B={wl.batch} H={wl.heads} D={wl.head_dim} INT{wl.bits} "
-          f"{wl.src} blocks={wl.blocks}", flush=True)
+          f"{wl.src} pack_mode {pack_mode} blocks={wl.blocks}", flush=True)
     for j in range(nb):
         kb, vb = vi.kv_block(wl, 0, "k", j), vi.kv_block(wl, 0, "v", j)
         q = vi.q_block(wl, 0, j)

@@ -2,6 +2,8 @@
 // Validates every argument on the host, computes the layout arithmetic and
 // launches the gfx950 kernels on the caller's stream.  Allocates nothing.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -94,7 +96,37 @@ int cache_ok(const kvq_cache_const& c) {
          aligned16(c.scale);
 }
 
-int device_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE; }
+// KVQ_DEBUG=1 in the environment: after every launch the call synchronizes
+// its stream (unless the stream is being captured into a graph) and checks
+// hipGetLastError, so a device fault or launch error is reported by the call
+// that caused it, on stderr and as KVQ_E_DEVICE.  Off by default.
+bool debug_mode() {
+  static const bool on = [] {
+    const char* v = getenv("KVQ_DEBUG");
+    return v && v[0] && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+int device_status(hipError_t e, hipStream_t stream, const char* call) {
+  if (e != hipSuccess) {
+    if (debug_mode()) fprintf(stderr, "kvq: %s: launch failed: %s\n", call, hipGetErrorString(e));
+    return KVQ_E_DEVICE;
+  }
+  if (debug_mode()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+      hipError_t s = hipStreamSynchronize(stream);
+      if (s == hipSuccess) s = hipGetLastError();
+      if (s != hipSuccess) {
+        fprintf(stderr, "kvq: %s: device error after the launch: %s\n", call,
+                hipGetErrorString(s));
+        return KVQ_E_DEVICE;
+      }
+    }
+  }
+  return KVQ_OK;
+}
 
 // threads per (tensor, b, h) tile and rows per thread for a block of n rows:
 // the smallest power-of-two group (>= one row of chunks) that covers the block
@@ -200,7 +232,8 @@ int make_attend_params(const kvq_layout* layout, int32_t block, const uint16_t* 
     p.bh_words = words_before(layout, layout->n_blocks);
     p.prefix_words = (int32_t)words_before(layout, block + 1);
     for (int i = 0; i < layout->n_blocks; ++i)
-      p.block_pad[i] = (int32_t)(cpw * words_before(layout, i) - layout->head_dim * offset_of(layout, i));
+      p.block_pad[i] =
+          (int32_t)(cpw * words_before(layout, i) - layout->head_dim * offset_of(layout, i));
   }
   return KVQ_OK;
 }
@@ -296,7 +329,8 @@ int kvq_quantize_block(const kvq_layout* layout, int32_t block, int32_t src_dtyp
                                    status_dev, &p);
   if (rc != KVQ_OK) return rc;
   return device_status(
-      launch_quantize(p, layout->head_dim, layout->bits, src_dtype == KVQ_F32, stream));
+      launch_quantize(p, layout->head_dim, layout->bits, src_dtype == KVQ_F32, stream), stream,
+      "kvq_quantize_block");
 }
 
 int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_rows,
@@ -307,7 +341,8 @@ int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_ro
     if (n_rows == 0) return KVQ_OK;
     if (!codes || !dst || !aligned16(codes) || !aligned16(dst)) return KVQ_E_INVAL;
     if (n_rows > kMaxElems / row_len) return KVQ_E_INVAL;
-    return device_status(launch_pack_words(codes, dst, n_rows * row_len, bits, stream));
+    return device_status(launch_pack_words(codes, dst, n_rows * row_len, bits, stream),
+                         stream, "kvq_pack");
   }
   if (pack_mode != 0) return KVQ_E_INVAL;
   const int32_t R = row_bytes(bits, row_len);
@@ -327,7 +362,7 @@ int kvq_pack(int32_t bits, int32_t pack_mode, const uint8_t* codes, int64_t n_ro
   p.n_chunks = n_rows * p.chunks_per_row;
   p.R = R;
   p.contiguous = (dst_row_stride == R) && (row_len % 8 == 0);
-  return device_status(launch_pack(p, stream));
+  return device_status(launch_pack(p, stream), stream, "kvq_pack");
 }
 
 int kvq_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_row_stride,
@@ -338,7 +373,8 @@ int kvq_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_
     if (n_rows == 0) return KVQ_OK;
     if (!codes || !src || !aligned16(codes) || !aligned16(src)) return KVQ_E_INVAL;
     if (n_rows > kMaxElems / row_len) return KVQ_E_INVAL;
-    return device_status(launch_unpack_words(src, codes, n_rows * row_len, bits, stream));
+    return device_status(launch_unpack_words(src, codes, n_rows * row_len, bits, stream),
+                         stream, "kvq_unpack");
   }
   if (pack_mode != 0) return KVQ_E_INVAL;
   if (src_row_stride < row_bytes(bits, row_len)) return KVQ_E_INVAL;
@@ -355,7 +391,7 @@ int kvq_unpack(int32_t bits, int32_t pack_mode, const uint8_t* src, int64_t src_
   p.bits = bits;
   p.chunks_per_row = (row_len + 7) / 8;
   p.n_chunks = n_rows * p.chunks_per_row;
-  return device_status(launch_unpack(p, stream));
+  return device_status(launch_unpack(p, stream), stream, "kvq_unpack");
 }
 
 int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const cache,
@@ -392,7 +428,7 @@ int kvq_dequantize(const kvq_layout* layout, int32_t n_filled, kvq_cache_const c
                                  layout->head_dim * offset_of(layout, i));
   }
   p.n_chunks = (int64_t)layout->batch * layout->heads * p.T_out * (p.D / 8);
-  return device_status(launch_dequantize(p, stream));
+  return device_status(launch_dequantize(p, stream), stream, "kvq_dequantize");
 }
 
 int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q_bf16,
@@ -401,7 +437,8 @@ int kvq_attend_packed(const kvq_layout* layout, int32_t block, const uint16_t* q
   AttendParams p;
   const int rc = make_attend_params(layout, block, q_bf16, k_cache, v_cache, scale, out, &p);
   if (rc != KVQ_OK) return rc;
-  return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+  return device_status(launch_attend(p, layout->head_dim, layout->bits, stream),
+                       stream, "kvq_attend_packed");
 }
 
 int kvq_attend_split_workspace(const kvq_layout* layout, int32_t block, int32_t max_splits,
@@ -425,11 +462,13 @@ int kvq_attend_packed_split(const kvq_layout* layout, int32_t block, const uint1
       workspace_bytes < split_workspace_bytes(layout, block, max_splits))
     return KVQ_E_INVAL;
   p.splits = pick_splits(p, max_splits);
-  if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+  if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream),
+                                          stream, "kvq_attend_packed_split");
   p.ws_rows = (int64_t)p.B * p.n * p.H;
   p.ws_o = static_cast<float*>(workspace);
   p.ws_ml = p.ws_o + (int64_t)p.splits * p.ws_rows * layout->head_dim;
-  return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream));
+  return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream),
+                       stream, "kvq_attend_packed_split");
 }
 
 int kvq_attend_packed_split_noalloc(const kvq_layout* layout, int32_t block,
@@ -443,13 +482,15 @@ int kvq_attend_packed_split_noalloc(const kvq_layout* layout, int32_t block,
   if (split_workspace_bytes(layout, block, max_splits) > KVQ_STATIC_SCRATCH_BYTES)
     return KVQ_E_INVAL;
   p.splits = pick_splits(p, max_splits);
-  if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream));
+  if (p.splits == 1) return device_status(launch_attend(p, layout->head_dim, layout->bits, stream),
+                                          stream, "kvq_attend_packed_split_noalloc");
   void* ws = device_scratch();
   if (!ws) return KVQ_E_DEVICE;
   p.ws_rows = (int64_t)p.B * p.n * p.H;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + (int64_t)p.splits * p.ws_rows * layout->head_dim;
-  return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream));
+  return device_status(launch_attend_split(p, layout->head_dim, layout->bits, stream),
+                       stream, "kvq_attend_packed_split_noalloc");
 }
 
 int kvq_quantize_attend(const kvq_layout* layout, int32_t block, int32_t src_dtype,
@@ -465,21 +506,22 @@ int kvq_quantize_attend(const kvq_layout* layout, int32_t block, int32_t src_dty
                           out, &ap);
   if (rc != KVQ_OK) return rc;
   return device_status(launch_quantize_attend(qp, ap, layout->head_dim, layout->bits,
-                                              src_dtype == KVQ_F32, stream));
+                                              src_dtype == KVQ_F32, stream),
+                                                  stream, "kvq_quantize_attend");
 }
 
 int kvq_stream_copy(const void* src, void* dst, uint64_t n_bytes, hipStream_t stream) {
   if (n_bytes % 16 != 0) return KVQ_E_INVAL;
   if (n_bytes == 0) return KVQ_OK;
   if (!src || !dst || !aligned16(src) || !aligned16(dst)) return KVQ_E_INVAL;
-  return device_status(launch_stream_copy(src, dst, n_bytes, stream));
+  return device_status(launch_stream_copy(src, dst, n_bytes, stream), stream, "kvq_stream_copy");
 }
 
 int kvq_stream_read(const void* src, uint64_t n_bytes, uint32_t* sink, hipStream_t stream) {
   if (n_bytes % 16 != 0) return KVQ_E_INVAL;
   if (n_bytes == 0) return KVQ_OK;
   if (!src || !sink || !aligned16(src)) return KVQ_E_INVAL;
-  return device_status(launch_stream_read(src, n_bytes, sink, stream));
+  return device_status(launch_stream_read(src, n_bytes, sink, stream), stream, "kvq_stream_read");
 }
 
 }  // extern "C"
