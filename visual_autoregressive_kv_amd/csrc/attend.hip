@@ -258,9 +258,11 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
   const int tensor = tid / GT;
   const int u = tid % GT;
   const int wt = u / kWave;
-  const int c = (wt % S::CW) * S::CPW + lane / L;
+  // (L and CW are powers of two: masks and shifts on the lane index)
+  constexpr int LSH = L == 8 ? 3 : 2;
+  const int c = (wt & (S::CW - 1)) * S::CPW + (lane >> LSH);
   const int rw = wt / S::CW;  // row wave
-  const int rg = rw * L + lane % L;
+  const int rg = rw * L + (lane & (L - 1));
   const int64_t row_stride = (int64_t)p.H * D;
   const int64_t base = ((int64_t)b * n * p.H + h) * D + 8 * c;
   const uint16_t* src = static_cast<const uint16_t*>(f.src[tensor]);
@@ -321,7 +323,7 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
   }
   float* red = scratch;                          // [tensor][row wave][min|max][D]
   float* zi = scratch + 2 * S::RW * 2 * D;       // [tensor][zero|reciprocal][D]
-  if (lane % L == 0) {
+  if ((lane & (L - 1)) == 0) {
     float* rm = red + ((tensor * S::RW + rw) * 2 + 0) * D + 8 * c;
     float* rx = red + ((tensor * S::RW + rw) * 2 + 1) * D + 8 * c;
     *reinterpret_cast<f32x4*>(rm) = f32x4{mn[0], mn[1], mn[2], mn[3]};
@@ -332,8 +334,9 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
   __syncthreads();
   int flags = 0;
   // the half's threads take one channel each (two for a 2-wave workgroup at
-  // head_dim 128)
-  for (int ch = u; ch < D; ch += GT) {
+  // head_dim 128; a straight branch otherwise, which keeps the register
+  // allocation of the tile loop free of spills)
+  auto channel_stats = [&](int ch) {
     float lo = red[((tensor * S::RW) * 2 + 0) * D + ch];
     float hi = red[((tensor * S::RW) * 2 + 1) * D + ch];
 #pragma unroll
@@ -355,6 +358,13 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
     zi[(tensor * 2 + 0) * D + ch] = gst.zf;
     zi[(tensor * 2 + 1) * D + ch] = gst.inv;
     if (tensor == 1) vover |= __builtin_fmaf(LEVELS, h2f(gst.sb), gst.zf) > 65504.0f;
+  };
+  if constexpr (D == kWave) {
+    if (u < kWave) channel_stats(lane);  // the half's first wave: lane = channel
+  } else if constexpr (GT >= D) {
+    if (u < D) channel_stats(u);
+  } else {
+    for (int ch = u; ch < D; ch += GT) channel_stats(ch);
   }
   __syncthreads();
   float zf[8], inv[8];
