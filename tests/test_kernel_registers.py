@@ -3,10 +3,10 @@ gfx950 assembly is compiled here, nothing runs).  The 4- and 8-wave kernels of
 the VAR shapes run at 4 waves per SIMD, which caps them at 128 VGPRs; at that
 cap a small change elsewhere in a kernel can move a spill into the key-tile
 loop, where its reload adds memory latency to every tile (one such move cost
-16% on the 100-token block).  Checked, for the head_dim-64 INT4 and INT3
-kernels that serve blocks of 65-256 tokens, fused and attention-only: the
-scratch accesses inside loops (none, or no more than the few some have always
-had), and the VGPR counts that keep them at 4 waves per SIMD."""
+16% on the 100-token block).  Checked, for the head_dim-64 2-, 4- and 8-wave
+kernels at every code width, fused and attention-only: the scratch accesses
+inside loops (none, or no more than the few some have always had), and the
+waves per SIMD their register counts allow."""
 import os
 import re
 import subprocess
@@ -54,17 +54,26 @@ def loop_scratch_ops(body):
 
 
 # attend_kernel<D, BITS, NW, FUSE, SPLIT, BW> -> scratch instructions allowed
-# inside loops: none for the kernels of the INT4 decode step and the 8-wave
-# kernels; the 4-wave INT3 and attention-only INT4 kernels carry a few reloads
-# (as they have since they were first built) and may not get more
-CASES = {(4, 8, 1): 0, (4, 8, 0): 0, (3, 8, 1): 0, (3, 8, 0): 0, (4, 4, 1): 0,
-         (4, 4, 0): 2, (3, 4, 1): 2, (3, 4, 0): 4}
+# inside loops: none, except the attention-only 2- and 4-wave INT4 kernels and
+# the 2- and 4-wave INT2 kernels, which carry the reloads they were built with
+# and may not get more.  And the waves per SIMD each keeps: 4 for 4- and 8-wave INT4
+# workgroups, 3 for 2-wave ones; one fewer for the 3- and 8-bit codes, which
+# hold two words per item in flight (at the INT4 caps they spilled in the loop).
+CASES = {}
+for bits in (2, 3, 4, 8):
+    two_words = bits in (3, 8)
+    for nw, occ in ((2, 3), (4, 4), (8, 4)):
+        for fuse in (0, 1):
+            loops = 2 if (bits in (2, 4) and nw in (2, 4) and fuse == 0) else 0
+            if bits == 2:  # INT2 at the INT4 caps: reloads in the 2- and 4-wave loops
+                loops = {2: 14 if fuse == 0 else 10, 4: 2, 8: 0}[nw]
+            CASES[(bits, nw, fuse)] = (loops, occ - (1 if two_words and nw != 8 else 0))
 
 
 @pytest.mark.parametrize("bits,nw,fuse", sorted(CASES))
 def test_no_spill_in_the_tile_loop(asm, bits, nw, fuse):
     name, body, info = kernel_body(asm, rf"attend_kernelILi64ELi{bits}ELi{nw}ELi{fuse}ELi0ELb0E")
-    assert loop_scratch_ops(body) <= CASES[(bits, nw, fuse)], name
-    vgpr = int(re.search(r"NumVgprs: (\d+)", info).group(1))
+    loops, min_occ = CASES[(bits, nw, fuse)]
+    assert loop_scratch_ops(body) <= loops, name
     occ = int(re.search(r"Occupancy: (\d+)", info).group(1))
-    assert vgpr <= 128 and occ >= 4, (name, vgpr, occ)
+    assert occ >= min_occ, (name, occ)

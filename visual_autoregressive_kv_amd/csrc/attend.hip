@@ -426,14 +426,22 @@ __device__ __forceinline__ void quantize_block_wg(const AttendParams& p, int b, 
 // SPLIT: the workgroup attends only key-tile range sp of p.splits (whole
 // tiles, balanced) and writes its unnormalized output, running maximum and
 // denominator to the workspace for attend_merge_kernel (attention only).
+// Register caps for residency: 2-wave workgroups at 3 waves per SIMD and 4-wave
+// workgroups at 4 (a few dwords spill; measured faster on VAR-d20 than the
+// extra dispatch rounds without the cap).  3- and 8-bit codes hold two words
+// per item in flight and spill inside the tile loop at those caps, so their 2-
+// and 4-wave workgroups run one wave per SIMD lower (measured faster: no spills).
+__host__ __device__ constexpr int waves_per_eu(int nw, int bits) {
+  const bool two_words = bits == 3 || bits == 8;
+  return nw == 2 ? (two_words ? 2 : 3) : nw == 4 ? (two_words ? 3 : 4) : 1;
+}
+
 // BW: the cache holds block-aligned 3-bit words (BITS == 3); each item's word
 // and shift are computed per tile from its key's block.
 template <int D, int BITS, int NW, int FUSE, int SPLIT = 0, bool BW = false>
-// Register caps chosen for residency: 2-wave workgroups at 3 waves per SIMD and
-// 4-wave workgroups at 4 (a few dwords spill; measured faster on VAR-d20 than
-// the extra dispatch rounds without the cap).
+// Register caps chosen for residency (waves_per_eu below).
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(NW == 2 ? 3 : NW == 4 ? 4 : 1))) void attend_kernel(AttendParams p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_eu(NW, BITS)))) void attend_kernel(AttendParams p) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;              // k-steps of the QK^T contraction
   constexpr int MT = D / 32;              // 32-row tiles of O^T
