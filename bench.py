@@ -20,7 +20,9 @@ step (query tokens x layers per second, quantize+pack included).  Per-kernel
 figures (`kernels`) come from HIP events on the launch stream over the timed
 steps: when every launch is of one kind (the fused VAR step) one event pair per
 step, otherwise events at every launch boundary; `per_block_us` are per-launch
-event spans (from a separate pass after the timed steps in the one-kind case).
+times of each block (in the one-kind case from a separate pass after the timed
+steps, with events only where the block changes: a block's span over its
+layers' back-to-back launches, divided by their number).
 `roofline` is for the kernel kind with the largest share of the step, over the
 launches of that kind (`blocks`); `cpu_baseline` is the CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
@@ -357,11 +359,17 @@ def main():
         roctx.roctxRangePop.restype = C.c_int
 
     def step(cs, events=None, mark=None):
-        """One decode step; events[c] before call c and events[c + 1] after it."""
+        """One decode step; events[c] before call c and events[c + 1] after it
+        (a list with every boundary, or a dict with some of them)."""
+        def record(k):
+            ev = events.get(k) if isinstance(events, dict) else events[k]
+            if ev is not None:
+                ev.record(stream)
+
         if mark is not None:
             roctx.roctxRangePushA(mark)
         if events is not None:
-            events[0].record(stream)
+            record(0)
         names = call_labels[id(cs)] if mark is not None else None
         for c, (_, _, fn, cargs) in enumerate(cs):
             if names is not None:
@@ -370,7 +378,7 @@ def main():
             if names is not None:
                 roctx.roctxRangePop()
             if events is not None:
-                events[c + 1].record(stream)
+                record(c + 1)
             if rc:
                 raise RuntimeError(f"kvq launch failed (rc={rc}) at call {c}")
         if mark is not None:
@@ -405,12 +413,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-launch spans: the timed events (several kinds) or a separate pass
+    # per-launch spans: the timed events (several kinds), or a separate pass
+    # with events where the block changes (a block's launches, one per layer,
+    # run back to back; an event between every two would add its own cost to
+    # each span)
     if single_kind:
-        span_evs = new_events(len(calls) + 1, args.steps)
+        bounds = [c for c in range(len(calls)) if c == 0 or calls[c][1] != calls[c - 1][1]]
+        bounds.append(len(calls))
+        blk_evs = [{c: torch.cuda.Event(enable_timing=True) for c in bounds}
+                   for _ in range(args.steps)]
         for s_ in range(args.steps):
-            step(calls, span_evs[s_])
+            step(calls, blk_evs[s_])
         torch.cuda.synchronize()
+        span_evs = None
     else:
         span_evs = evs
 
@@ -419,9 +434,12 @@ def main():
                   "fused": lambda w, k: quant_bytes(w, k) + attend_bytes(w, k)}
 
     def kind_totals(cs, span, steps):
+        """Per kind: event time (0 without span events), launches, bytes, flops;
+        per kind and block: the per-launch times."""
         kinds, per_block = {}, {}
         for c, (kind, j, _, _) in enumerate(cs):
-            ms = sum(span[s_][c].elapsed_time(span[s_][c + 1]) for s_ in range(steps))
+            ms = (sum(span[s_][c].elapsed_time(span[s_][c + 1]) for s_ in range(steps))
+                  if span is not None else 0.0)
             k = kinds.setdefault(kind, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0,
                                         "tokens": 0})
             k["ms"] += ms
@@ -437,6 +455,10 @@ def main():
     if single_kind:  # the kind's time is the timed steps' span
         only = kinds[calls[0][0]]
         only["ms"] = sum(e[0].elapsed_time(e[1]) for e in evs)
+        per_block = {calls[0][0]: {}}
+        for a, z in zip(bounds[:-1], bounds[1:]):
+            ms = sum(blk_evs[s_][a].elapsed_time(blk_evs[s_][z]) for s_ in range(args.steps))
+            per_block[calls[0][0]][calls[a][1]] = [ms / args.steps / (z - a)]
     per_block_us = {kind: [round(1e3 * sum(v) / len(v), 2) for _, v in sorted(d.items())]
                     for kind, d in per_block.items()}
     per_block_blocks = {kind: sorted(d) for kind, d in per_block.items()}
@@ -521,7 +543,9 @@ def main():
         "passes": passes,
         "copy_peak_GBps": round(copy_gbps, 1),
         "read_peak_GBps": round(read_gbps, 1),
-        "timing": ("one event pair per timed step; per-block spans from a separate pass"
+        "timing": ("one event pair per timed step; per-block spans from a separate pass with "
+                   "events where the block changes (a block's span over its layers' launches "
+                   "divided by their number)"
                    if single_kind else "events at every launch boundary of the timed steps"),
         "per_block_us": per_block_us,
         "roofline": roofline,

@@ -58,9 +58,19 @@ def decode_both_ways(oracle, wl, layer=0, scale=0.0):
     vi.Workload("d128_int3_rope", 1, 2, 3, 128, 3, vi.VAR_BLOCKS, "bf16", rope=True, seed=103),
     vi.Workload("d128_int2", 1, 2, 3, 128, 2, (7, 40, 97, 200), "bf16", seed=107),
     vi.Workload("d128_int8", 1, 2, 3, 128, 8, (7, 40, 97, 200), "bf16", seed=109),
+    # the 8-wave fused kernel after long cached prefixes (129-256 tokens from
+    # key tile 5 on) at every width, with ragged block and prefix ends, and
+    # with 16 and 17 blocks of statistics in LDS
+    vi.Workload("ovl_int3", 1, 2, 3, 64, 3, (160, 129, 255, 256), "bf16", seed=111),
+    vi.Workload("ovl_int8_rope", 1, 2, 3, 64, 8, (1, 170, 193, 131), "bf16", rope=True,
+                seed=113),
+    vi.Workload("ovl_int2", 1, 2, 3, 64, 2, (161, 250), "bf16", seed=115),
+    vi.Workload("ovl_16_blocks", 1, 2, 3, 64, 4, (10,) * 14 + (20, 140), "bf16", seed=117),
+    vi.Workload("ovl_17_blocks", 1, 2, 3, 64, 4, (10,) * 16 + (140,), "bf16", seed=119),
 ], ids=["tiny_f32", "d20_int4", "d20_int3_rope", "d24_int4", "edge_int3", "edge_d128",
         "many_blocks", "int2", "int8_rope", "int8_f32", "d128_int4", "d128_int3_rope",
-        "d128_int2", "d128_int8"])
+        "d128_int2", "d128_int8", "ovl_int3", "ovl_int8_rope", "ovl_int2", "ovl_16_blocks",
+        "ovl_17_blocks"])
 def test_fused_matches_two_calls_and_oracle(oracle, wl):
     kf, vf, ks, vs, ko, vo, steps = decode_both_ways(oracle, wl)
     assert_cache_equal(kf, ko, "fused K")
@@ -121,13 +131,16 @@ def test_fused_full_batch_every_block(oracle):
     assert_cache_equal(vf, vo, "fused V")
 
 
-@pytest.mark.parametrize("src,second,head_dim", [("bf16", 16, 64), ("f32", 16, 64),
-                                                 ("bf16", 64, 64), ("bf16", 200, 64),
-                                                 ("bf16", 64, 128), ("bf16", 200, 128)])
-def test_fused_status_flags(oracle, src, second, head_dim):
+@pytest.mark.parametrize("src,second,head_dim,first", [
+    ("bf16", 16, 64, 16), ("f32", 16, 64, 16), ("bf16", 64, 64, 16), ("bf16", 200, 64, 16),
+    ("bf16", 64, 128, 16), ("bf16", 200, 128, 16),
+    # a 200-token block after 192 cached keys
+    ("bf16", 200, 64, 192)])
+def test_fused_status_flags(oracle, src, second, head_dim, first):
     """Input screening through the fused call: the one-wave path (16 tokens) and
-    the workgroup path (64 and 200 tokens, head_dim 64 and 128)."""
-    wl = vi.Workload("status", 1, 2, 3, head_dim, 4, (16, second), src, seed=5)
+    the workgroup path (64 and 200 tokens, head_dim 64 and 128, after a short
+    and a long cached prefix)."""
+    wl = vi.Workload("status", 1, 2, 3, head_dim, 4, (first, second), src, seed=5)
     Lg, _ = layouts(oracle, wl)
     k0, v0 = vi.kv_block(wl, 0, "k", 0), vi.kv_block(wl, 0, "v", 0)
     kb, vb = vi.kv_block(wl, 0, "k", 1), vi.kv_block(wl, 0, "v", 1)

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import varq_inputs as vi
 import visual_autoregressive_kv_amd as K
 from gpu_common import DEV, assert_cache_equal, check_attn, to_dev
 
@@ -39,9 +40,14 @@ def edge_block(rng, B, n, H, D, tensor):
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-@pytest.mark.parametrize("blocks", [(1, 4, 9, 16, 25), (5, 40, 33), (700, 300)],
-                         ids=["short", "workgroup", "key_ranges"])
-def test_binary16_edge_groups(oracle, bits, blocks):
+@pytest.mark.parametrize("blocks,bf16_from", [((1, 4, 9, 16, 25), None), ((5, 40, 33), None),
+                                              ((700, 300), None), ((170, 180), 1)],
+                         ids=["short", "workgroup", "key_ranges", "bf16_after_edges"])
+def test_binary16_edge_groups(oracle, bits, blocks, bf16_from):
+    """bf16_from: the first block given as bf16 (N(0, 1) values, no edge groups;
+    bf16 input cannot reach a top level above 65504, since its largest value
+    below 65504 is 65280): the fused call then takes its workgroup kernels
+    (here the 8-wave one), with v_hat halved for the cached edge groups."""
     B, H, D = 2, 3, 64
     rng = np.random.default_rng(1000 + 10 * bits + len(blocks))
     Lg = K.make_layout(B, H, D, bits, blocks)
@@ -51,7 +57,11 @@ def test_binary16_edge_groups(oracle, bits, blocks):
     ko, vo = oracle.alloc_cache(Lo), oracle.alloc_cache(Lo)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     for j, n in enumerate(blocks):
-        kb, vb = edge_block(rng, B, n, H, D, "k"), edge_block(rng, B, n, H, D, "v")
+        if bf16_from is not None and j >= bf16_from:
+            kb = vi.f32_to_bf16_bits(rng.standard_normal((B, n, H, D)).astype(np.float32))
+            vb = vi.f32_to_bf16_bits(rng.standard_normal((B, n, H, D)).astype(np.float32))
+        else:
+            kb, vb = edge_block(rng, B, n, H, D, "k"), edge_block(rng, B, n, H, D, "v")
         qf = rng.standard_normal((B, n, H, D)).astype(np.float32)
         # head 1 holds the K edge groups: its queries are scaled by 2^-10 (exact)
         # so that its scores stay in the range the accuracy bound covers
