@@ -12,6 +12,8 @@
 //                 other LDS buffer while those MFMAs run,
 //                 softmax and O of tile j,
 //                 one barrier.
+//   (8-wave workgroups stagger this order between the two waves that share a
+//   SIMD, so that one's VALU work runs beside the other's MFMAs.)
 //   Dequantization (shared by the workgroup's waves through LDS):
 //   - the (block, channel) statistics of the whole prefix are staged in LDS;
 //     every thread owns fixed items (one key x 8 channels of K or of V) and
@@ -712,6 +714,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW, BITS)))) void attend_kernel(
     issue_loads(j + 2, nxt, nxt2, nxtsh);  // unconditional: past the prefix it reads nothing
 
     if (wave_live) {
+      // Phase stagger (8-wave workgroups): waves w and w + 4 share a SIMD and
+      // would otherwise reach a tile's MFMA and VALU phases together.  The upper
+      // half dequantizes tile j + 1 before its QK^T, so its VALU work runs beside
+      // the lower half's MFMAs; at head_dim 64 the lower half dequantizes after
+      // its PV (at 128, whose QK^T is twice as long, beside its own QK^T MFMAs).
+      // Every wave's arithmetic is unchanged, only its order.
+      const bool dq_first = NW == 8 && wave >= NW / 2;
+      const bool dq_last = NW == 8 && D == 64 && wave < NW / 2;
+      if (dq_first && has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
       // ---- S^T = K_hat Q^T -------------------------------------------------
       f32x16 s = f32x16{};
       bf16x8 ah[2], al[2];  // operands of the current and the next k-step
@@ -735,7 +746,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW, BITS)))) void attend_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // the next tile's dequantization runs while these MFMAs complete
-      if (has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
+      if (!dq_first && !dq_last && has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
 
       // ---- online softmax (log2 domain) -----------------------------------
       if (t0 + KT > n_prefix) {
@@ -786,6 +797,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu(NW, BITS)))) void attend_kernel(
                                                          o[i], 0, 0, 0);
         }
       }
+      if (dq_last && has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
     }
 
     if (!wave_live && has_next) dequant(j + 1, buf ^ 1, cur, cur2, cursh);
