@@ -1,7 +1,8 @@
 """VAR-Q packed KV cache for MI355X (gfx950).
 
 The hot path -- (block, channel) min/max quantization of each decoded block,
-INT4/INT3 bit-packing, and block-causal attention over the packed cache -- runs
+2-, 3-, 4- or 8-bit packing (dense rows, or block-aligned 3-bit words), and
+block-causal attention over the packed cache -- runs
 in the HIP kernels of libkvq.so behind the C ABI of include/kvq.h.  The
 functions below are its thin Python binding (torch supplies device memory and
 streams only).
