@@ -56,5 +56,5 @@ def pytest_terminal_summary(terminalreporter):
     tr.write_line(f"attention error vs the binary64 oracle ({len(gc.ERR_LOG)} checks; bound 2e-3 "
                   "per call and per (b,h); per channel reported only):")
     for key, (n, e, ebh, ech) in sorted(fam.items()):
-        ch = "sampled" if ech is None else f"{ech:.2e}"
+        ch = "n/a" if ech is None else f"{ech:.2e}"
         tr.write_line(f"  {key:<48} n={n:<3} per call {e:.2e}  per (b,h) {ebh:.2e}  per channel {ch}")

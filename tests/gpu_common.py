@@ -1,5 +1,8 @@
 """Shared helpers of the GPU parity tests: feed the same seeded inputs to the
 HIP library and to the CPU oracle and bring results back for comparison."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -50,6 +53,45 @@ def fill_both(oracle, wl, layer=0, upto=None, status=None, pack_mode=0):
     return Lg, Lo, kg, vg, ko, vo
 
 
+def oracle_threads() -> int:
+    """Host threads for the oracle: this process's cores, capped by OMP_NUM_THREADS
+    when the host sets it (the GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+def oracle_attend_batch(oracle, Lo, block, q, k_cache, v_cache, scale=0.0):
+    """The oracle's whole attention output [B][n][H][D], its (sequence, head) pairs
+    split over host threads.  Each pair is handed to the oracle as a sequence of
+    its own (batch B*H, one head): the caches' [B][H][...] arrays already have
+    that layout, and the queries are transposed to [B*H][n][1][D].  The oracle
+    attends every (sequence, head) on its own, so the values are those of one
+    call on the original layout; each thread's call writes only its own rows
+    (the oracle is single-threaded and releases the interpreter lock)."""
+    B, H = Lo.batch, Lo.heads
+    blocks = [Lo.block_tokens[i] for i in range(Lo.n_blocks)]
+    L1 = oracle.make_layout(B * H, 1, Lo.head_dim, Lo.bits, blocks, Lo.pack_mode)
+
+    def pairs(c):  # [B][H][...] -> [B*H][1][...], same memory
+        return {k: np.ascontiguousarray(v).reshape((B * H, 1) + v.shape[2:]) for k, v in c.items()}
+
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    n, D = q.shape[1], q.shape[3]
+    q1 = np.ascontiguousarray(q.transpose(0, 2, 1, 3)).reshape(B * H, n, 1, D)
+    out1 = np.zeros(q1.shape, np.float32)
+    k1, v1 = pairs(k_cache), pairs(v_cache)
+    t = min(oracle_threads(), B * H)
+    cuts = [B * H * i // t for i in range(t + 1)]
+    with ThreadPoolExecutor(t) as ex:
+        list(ex.map(lambda i: oracle.attend(L1, block, q1, k1, v1, scale=scale,
+                                            b0=cuts[i], b1=cuts[i + 1], out=out1), range(t)))
+    return out1.reshape(B, H, n, D).transpose(0, 2, 1, 3).astype(np.float64)
+
+
 def assert_cache_equal(g, o, what=""):
     gh = cache_to_host(g)
     for key in ("zero", "scale", "codes"):
@@ -95,24 +137,3 @@ def check_attn(got: np.ndarray, ref: np.ndarray, what: str = "", tol: float = AT
     assert e <= tol, (what, e)
     assert ebh <= tol, (what, "per (b,h)", ebh)
     return e, ebh, ech
-
-
-def check_rows(got_rows: np.ndarray, ref_rows: np.ndarray, picks, what: str = "",
-               tol: float = ATTN_TOL):
-    """Sampled output rows (one (b, i, h) per pick) against single-row oracle
-    evaluations: the per-call bound over the sample, and the per-(b, h) bound with
-    each (b, h) normalized by the largest |ref| among its sampled rows (no larger
-    than the whole (b, h)'s, so the check is at least as strict)."""
-    assert np.isfinite(got_rows).all(), f"{what}: non-finite output"
-    d = np.abs(got_rows.astype(np.float64) - ref_rows)
-    e = float(d.max() / np.abs(ref_rows).max())
-    groups = {}
-    for r, (b, _, h) in enumerate(picks):
-        groups.setdefault((b, h), []).append(r)
-    ebh = max(float(d[rows].max() / np.abs(ref_rows[rows]).max()) for rows in groups.values())
-    print(f"[attn] {what}: sampled rows {len(picks)}, err per call {e:.2e}, per (b,h) {ebh:.2e}",
-          flush=True)
-    ERR_LOG.append((what, e, ebh, None))
-    assert e <= tol, (what, e)
-    assert ebh <= tol, (what, "per (b,h)", ebh)
-    return e, ebh
